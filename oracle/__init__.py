@@ -1,0 +1,154 @@
+"""fp64 CPU oracle for the attention forward -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product library never uses it.
+
+It wraps ``attn_oracle.c`` (plain C, fp64, two-pass softmax over a
+materialised score row). See that file's header for the definition it writes
+out and the pages it follows. Inputs are numpy ``uint16`` arrays holding raw
+fp16 or bf16 bit patterns, contiguous ``[B, H, S, D]``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_DTYPES = {"f16": 0, "bf16": 1}
+_MASKS = {"full": 0, "causal": 1, "window": 2}
+
+_i64 = ctypes.c_int64
+_ptr = ctypes.c_void_p
+
+
+def _bind(lib):
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_visible.argtypes = [_i64, _i64, ctypes.c_int, _i64, _i64]
+    lib.oracle_visible.restype = ctypes.c_int
+    lib.oracle_pair_count.argtypes = [_i64, ctypes.c_int, _i64, _i64]
+    lib.oracle_pair_count.restype = _i64
+    lib.oracle_attention_rows.argtypes = [
+        _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int,
+        _i64, _i64, ctypes.c_int, _i64, _ptr, _ptr, _ptr, ctypes.c_int]
+    lib.oracle_attention_rows.restype = ctypes.c_int
+    lib.oracle_attention_probs.argtypes = [
+        _ptr, _ptr, _ptr, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64, _i64,
+        ctypes.c_int, _ptr, _ptr, _ptr]
+    lib.oracle_attention_probs.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [_ptr, _i64, ctypes.c_int, _ptr]
+    lib.oracle_decode.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+class Oracle:
+    """One loaded build of the oracle (the real one, or a planted-mistake copy)."""
+
+    def __init__(self, path):
+        self.path = path
+        self.lib = _bind(ctypes.CDLL(path))
+
+    # -- masks ---------------------------------------------------------------
+    @staticmethod
+    def _mask_args(mask, window):
+        if mask not in _MASKS:
+            raise ValueError(f"mask must be one of {sorted(_MASKS)}, got {mask!r}")
+        wl, wr = window if window is not None else (-1, -1)
+        return _MASKS[mask], int(wl), int(wr)
+
+    def visible(self, i, j, mask, window=(-1, -1)):
+        m, wl, wr = self._mask_args(mask, window)
+        return bool(self.lib.oracle_visible(i, j, m, wl, wr))
+
+    def pair_count(self, S, mask, window=(-1, -1)):
+        """Visible (i, j) pairs of one S x S head, by enumeration."""
+        m, wl, wr = self._mask_args(mask, window)
+        return int(self.lib.oracle_pair_count(S, m, wl, wr))
+
+    # -- decoding ------------------------------------------------------------
+    def decode(self, bits, dtype):
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, dtype=np.float64)
+        self.lib.oracle_decode(bits.ctypes.data, bits.size, _DTYPES[dtype], out.ctypes.data)
+        return out
+
+    # -- attention -----------------------------------------------------------
+    def attention_rows(self, q, k, v, dtype, scale, mask, window=(-1, -1), rows=None,
+                       nthreads=0):
+        """fp64 output rows and LSE for the flat row indices ``rows``.
+
+        ``q, k, v``: uint16 bit patterns, shape [B, H, S, D]. ``rows``: flat
+        indices ``(b*H + h)*S + i`` (default: every row). Returns
+        ``(o [n, D] float64, lse [n] float64)``.
+        """
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+        if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+            raise ValueError("q, k, v must share one [B, H, S, D] shape")
+        B, H, S, D = q.shape
+        if rows is None:
+            rows = np.arange(B * H * S, dtype=np.int64)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        m, wl, wr = self._mask_args(mask, window)
+        o = np.empty((rows.size, D), dtype=np.float64)
+        lse = np.empty(rows.size, dtype=np.float64)
+        rc = self.lib.oracle_attention_rows(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, S, D, float(scale), m,
+            wl, wr, _DTYPES[dtype], rows.size, rows.ctypes.data, o.ctypes.data,
+            lse.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_attention_rows rejected its arguments")
+        return o, lse
+
+    def attention(self, q, k, v, dtype, scale, mask, window=(-1, -1), nthreads=0):
+        """Every row: ``(o [B,H,S,D] float64, lse [B,H,S] float64)``."""
+        B, H, S, D = q.shape
+        o, lse = self.attention_rows(q, k, v, dtype, scale, mask, window, None, nthreads)
+        return o.reshape(B, H, S, D), lse.reshape(B, H, S)
+
+    def attention_probs(self, qh, kh, vh, dtype, scale, mask, window=(-1, -1)):
+        """One head with its [S, S] probability matrix: ``(p, o, lse)``."""
+        qh = np.ascontiguousarray(qh, dtype=np.uint16)
+        kh = np.ascontiguousarray(kh, dtype=np.uint16)
+        vh = np.ascontiguousarray(vh, dtype=np.uint16)
+        S, D = qh.shape
+        m, wl, wr = self._mask_args(mask, window)
+        p = np.empty((S, S), dtype=np.float64)
+        o = np.empty((S, D), dtype=np.float64)
+        lse = np.empty(S, dtype=np.float64)
+        rc = self.lib.oracle_attention_probs(
+            qh.ctypes.data, kh.ctypes.data, vh.ctypes.data, S, D, float(scale), m, wl, wr,
+            _DTYPES[dtype], p.ctypes.data, o.ctypes.data, lse.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_attention_probs rejected its arguments")
+        return p, o, lse
+
+    def max_threads(self):
+        return int(self.lib.oracle_max_threads())
+
+
+_default = None
+
+
+def load(rebuild=False):
+    """The oracle, built from source first if no build exists yet."""
+    global _default
+    if _default is None or rebuild:
+        path = _build.lib_path()
+        if rebuild or not os.path.exists(path):
+            _build.build()
+        _default = Oracle(path)
+    return _default
+
+
+def load_planted(plant):
+    """A copy of the oracle with deliberate mistake ``plant`` built in (tests only)."""
+    path = _build.lib_path(plant)
+    _build.build(plant=plant, out=path)
+    return Oracle(path)

@@ -1,0 +1,309 @@
+/*
+ * attn_oracle.c -- plain fp64 CPU oracle for the attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY. The product library never links, loads or calls
+ * this file. Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it. It shares no code, header, table or constant with the GPU path.
+ *
+ * What it computes is the plain definition of softmax attention, not the
+ * tiled method. All four pages state that the tiled method reaches exactly
+ * this result (up to rounding order), so the oracle is that definition written
+ * out:
+ *   - Ascend C FlashAttention-2 tile-fusion page (ascendai.csdn.net),
+ *     section 1.1 (scores, row softmax, product with V) and section 1.2
+ *     (the tiled rewrite is mathematically the same result);
+ *   - ops-transformer FlashAttention walkthrough (hwcomputing.csdn.net,
+ *     6a0ef689), "core idea: tiling + online softmax" (S = QK^T, P =
+ *     softmax(S), O = PV over [B,H,S,D] tensors);
+ *   - catlass FlashAttention article (lnwmold.com/news/1200460), section
+ *     "background" (same result as standard attention) and section "usage"
+ *     (full / causal / (window_left, window_right) masks);
+ *   - "FlashAttention on Ascend NPU: from principle to practice" page
+ *     (hwcomputing.csdn.net, 6a0fe629), section "core idea: IO-aware"
+ *     (standard attention divides QK^T by sqrt(head_dim) before softmax).
+ *
+ * For every batch b, head h and query row i:
+ *   s_ij = scale * sum_d q[b,h,i,d] * k[b,h,j,d]  if key j is visible from i,
+ *          -inf                                    otherwise;
+ *   m_i  = max_j s_ij                               (pass 1);
+ *   e_ij = exp(s_ij - m_i),  l_i = sum_j e_ij       (pass 2);
+ *   o[b,h,i,:] = (sum_j e_ij * v[b,h,j,:]) / l_i;
+ *   lse[b,h,i] = m_i + log(l_i)   (natural log of sum_j exp(s_ij)).
+ * A row with no visible key (none exists for the three mask modes, since
+ * j = i is always visible) is defined as o = 0, lse = -inf.
+ *
+ * Inputs are raw 16-bit patterns (IEEE binary16 or bfloat16) in contiguous
+ * row-major [B,H,S,D] order. Everything after decoding is fp64; exp and log
+ * are the C library's double routines.
+ *
+ * Readings of points the pages leave open are listed with each function.
+ *
+ * ORACLE_PLANT (compile-time, tests only): when defined to a nonzero value,
+ * one deliberate mistake is built in, so the test suite can show that its
+ * pins catch it. The default build defines nothing and is the oracle.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef ORACLE_PLANT
+#define ORACLE_PLANT 0
+#endif
+
+/* Element encodings accepted by the oracle (its own codes). */
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+/* Mask modes (its own codes): catlass article, section "usage". */
+enum { ORACLE_FULL = 0, ORACLE_CAUSAL = 1, ORACLE_WINDOW = 2 };
+
+/* IEEE 754 binary16 -> double, exact: 1 sign bit, 5 exponent bits (bias 15),
+ * 10 fraction bits; exponent 0 encodes zero/subnormals, 31 encodes inf/NaN. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1f;
+    int fr = h & 0x3ff;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -24);              /* fr * 2^(1-15-10) */
+    else if (ex == 31)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(fr | 0x400), ex - 25); /* (1024+fr) * 2^(ex-15-10) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double, exact: a bfloat16 is the upper half of an IEEE binary32. */
+double oracle_bf16_to_f64(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double decode(uint16_t x, int dtype)
+{
+    return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(x) : oracle_f16_to_f64(x);
+}
+
+/* Is key j visible from query i?
+ *   full:   always (catlass article, "usage": no mask).
+ *   causal: j <= i. The Ascend C tile-fusion page, section 4.2, masks a key
+ *           exactly when its position is after the query's, so the diagonal
+ *           stays visible.
+ *   window: i - wl <= j <= i + wr, both ends inclusive; a negative bound means
+ *           that side is unbounded. The catlass article ("usage") only names a
+ *           (window_left, window_right) pair; this inclusive reading makes
+ *           (-1, 0) the causal mask and (-1, -1) the full mask. */
+int oracle_visible(int64_t i, int64_t j, int mask_mode, int64_t wl, int64_t wr)
+{
+    switch (mask_mode) {
+    case ORACLE_FULL:
+        return 1;
+    case ORACLE_CAUSAL:
+#if ORACLE_PLANT == 2
+        return j < i;                    /* planted: diagonal dropped */
+#else
+        return j <= i;
+#endif
+    case ORACLE_WINDOW: {
+#if ORACLE_PLANT == 3
+        int left_ok = wl < 0 || j > i - wl;   /* planted: left edge exclusive */
+#else
+        int left_ok = wl < 0 || j >= i - wl;
+#endif
+        int right_ok = wr < 0 || j <= i + wr;
+        return left_ok && right_ok;
+    }
+    default:
+        return 0;
+    }
+}
+
+/* Number of visible (i, j) pairs of one S x S head, by enumeration. */
+int64_t oracle_pair_count(int64_t S, int mask_mode, int64_t wl, int64_t wr)
+{
+    int64_t total = 0;
+#pragma omp parallel for reduction(+ : total) schedule(static)
+    for (int64_t i = 0; i < S; ++i)
+        for (int64_t j = 0; j < S; ++j)
+            total += oracle_visible(i, j, mask_mode, wl, wr);
+    return total;
+}
+
+static int check_args(int64_t B, int64_t H, int64_t S, int64_t D, int mask_mode, int dtype)
+{
+    if (B < 0 || H < 0 || S < 0 || D <= 0) return -1;
+    if (mask_mode < ORACLE_FULL || mask_mode > ORACLE_WINDOW) return -1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    return 0;
+}
+
+/* One query row of one head: materialise the score row, then two passes.
+ * qh, kh, vh point at the head's [S, D] block. srow (S doubles), qrow and
+ * orow (D doubles each) are scratch owned by the caller. */
+static void one_row(const uint16_t *qh, const uint16_t *kh, const uint16_t *vh,
+                    int64_t S, int64_t D, double scale, int mask_mode, int64_t wl,
+                    int64_t wr, int dtype, int64_t i, double *srow, double *qrow,
+                    double *orow, double *o_out, double *lse_out)
+{
+    for (int64_t d = 0; d < D; ++d)
+        qrow[d] = decode(qh[i * D + d], dtype);
+
+    /* Scores (Ascend C tile-fusion page, section 1.1; the NPU optimisation
+     * page, section "core idea: IO-aware": QK^T times the scale). Masked
+     * entries are -inf and need no dot product. */
+    for (int64_t j = 0; j < S; ++j) {
+        if (!oracle_visible(i, j, mask_mode, wl, wr)) {
+            srow[j] = -INFINITY;
+            continue;
+        }
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc += qrow[d] * decode(kh[j * D + d], dtype);
+#if ORACLE_PLANT == 1
+        srow[j] = acc;                   /* planted: scale dropped */
+#elif ORACLE_PLANT == 4
+        srow[j] = -scale * acc;          /* planted: sign flipped */
+#else
+        srow[j] = scale * acc;
+#endif
+    }
+
+    /* Pass 1: row maximum. */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < S; ++j)
+        if (srow[j] > m) m = srow[j];
+
+    if (m == -INFINITY) {                 /* no visible key */
+        for (int64_t d = 0; d < D; ++d) o_out[d] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+
+    /* Pass 2: exponentials, their sum, and the weighted sum of V rows. */
+    for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+    double l = 0.0;
+    for (int64_t j = 0; j < S; ++j) {
+        if (srow[j] == -INFINITY) continue;        /* exp(-inf) = 0 */
+        double e = exp(srow[j] - m);
+        l += e;
+#if ORACLE_PLANT == 5
+        int64_t jv = (j + 1 < S) ? j + 1 : j;      /* planted: wrong V row */
+#else
+        int64_t jv = j;
+#endif
+        for (int64_t d = 0; d < D; ++d)
+            orow[d] += e * decode(vh[jv * D + d], dtype);
+    }
+    for (int64_t d = 0; d < D; ++d) o_out[d] = orow[d] / l;
+#if ORACLE_PLANT == 6
+    *lse_out = m + log2(l);               /* planted: wrong logarithm base */
+#else
+    *lse_out = m + log(l);
+#endif
+}
+
+/* Selected rows of a [B,H,S,D] problem.
+ * rows[r] is a flat row index (b*H + h)*S + i; o is [n_rows, D] and lse is
+ * [n_rows], both fp64. nthreads <= 0 uses the OpenMP default.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                          int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                          int mask_mode, int64_t wl, int64_t wr, int dtype,
+                          int64_t n_rows, const int64_t *rows, double *o, double *lse,
+                          int nthreads)
+{
+    if (check_args(B, H, S, D, mask_mode, dtype)) return -1;
+    int64_t total_rows = B * H * S;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= total_rows) return -1;
+    if (n_rows == 0) return 0;
+
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+    {
+        double *srow = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)D);
+        double *orow = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!srow || !qrow || !orow) {
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t bh = rows[r] / S;
+                int64_t i = rows[r] % S;
+                const int64_t base = bh * S * D;
+                one_row(q + base, k + base, v + base, S, D, scale, mask_mode, wl, wr,
+                        dtype, i, srow, qrow, orow, o + r * D, lse + r);
+            }
+        }
+        free(srow);
+        free(qrow);
+        free(orow);
+    }
+    return failed ? -1 : 0;
+}
+
+/* One whole head with the probability matrix materialised: p is [S, S] with
+ * p[i, j] = exp(s_ij - m_i) / l_i, o is [S, D], lse is [S]. Small S only
+ * (the S x S matrix is what the tiled method avoids writing). */
+int oracle_attention_probs(const uint16_t *qh, const uint16_t *kh, const uint16_t *vh,
+                           int64_t S, int64_t D, double scale, int mask_mode, int64_t wl,
+                           int64_t wr, int dtype, double *p, double *o, double *lse)
+{
+    if (check_args(1, 1, S, D, mask_mode, dtype)) return -1;
+    double *qrow = (double *)malloc(sizeof(double) * (size_t)D);
+    double *orow = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!qrow || !orow) {
+        free(qrow);
+        free(orow);
+        return -1;
+    }
+    for (int64_t i = 0; i < S; ++i) {
+        double *srow = p + i * S;
+        one_row(qh, kh, vh, S, D, scale, mask_mode, wl, wr, dtype, i, srow, qrow, orow,
+                o + i * D, lse + i);
+        /* one_row leaves the scores in srow; turn them into probabilities. */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < S; ++j)
+            if (srow[j] > m) m = srow[j];
+        if (m == -INFINITY) {
+            for (int64_t j = 0; j < S; ++j) srow[j] = 0.0;
+            continue;
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < S; ++j)
+            l += (srow[j] == -INFINITY) ? 0.0 : exp(srow[j] - m);
+        for (int64_t j = 0; j < S; ++j)
+            srow[j] = (srow[j] == -INFINITY) ? 0.0 : exp(srow[j] - m) / l;
+    }
+    free(qrow);
+    free(orow);
+    return 0;
+}
+
+/* Decode n raw 16-bit values to fp64 with the oracle's own decoders. */
+void oracle_decode(const uint16_t *x, int64_t n, int dtype, double *out)
+{
+    for (int64_t t = 0; t < n; ++t) out[t] = decode(x[t], dtype);
+}
+
+/* Threads the oracle will use by default (reported by the CPU baseline). */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

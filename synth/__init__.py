@@ -1,0 +1,91 @@
+"""Seeded synthetic inputs for the attention forward.
+
+This module only draws and encodes inputs; it holds none of the attention
+arithmetic. Both the GPU path's tests/benchmark and the CPU oracle receive the
+same bytes from here.
+
+Recipe (every workload):
+  * ``numpy.random.default_rng(seed)`` (PCG64);
+  * ``standard_normal(dtype=float32)`` in C order, drawn in the order q, k, v,
+    each of shape [B, H, S, D];
+  * optional large-logit outliers: for each (b, h) in order, ``round(frac*S)``
+    distinct key rows picked with ``rng.choice(S, n, replace=False)`` are
+    multiplied by ``outlier_scale`` in fp32 (before the single rounding);
+  * one rounding to the storage type, round-to-nearest-even: fp16 through
+    numpy's IEEE conversion, bf16 by integer rounding of the fp32 bit pattern.
+Arrays come back as ``uint16`` bit patterns, contiguous [B, H, S, D].
+"""
+import hashlib
+
+import numpy as np
+
+# Workloads of the forward pass: shapes, masks, scales and seeds. The
+# B4 H32 S4096 D128 fp16 shape is the one the catlass FlashAttention article
+# benchmarks (section "performance data"); the sliding-window rows use a
+# window that is, and one that is not, a multiple of a 64-key tile.
+WORKLOADS = {
+    "tiny_full":   dict(B=1, H=2, S=128, D=64, dtype="f16", mask="full",
+                        window=(-1, -1), scale=0.125, seed=1),
+    "tiny_causal": dict(B=1, H=2, S=128, D=64, dtype="f16", mask="causal",
+                        window=(-1, -1), scale=0.125, seed=1),
+    "d64_causal":  dict(B=1, H=32, S=2048, D=64, dtype="f16", mask="causal",
+                        window=(-1, -1), scale=0.125, seed=2),
+    "b4h32s4096_full":   dict(B=4, H=32, S=4096, D=128, dtype="f16", mask="full",
+                              window=(-1, -1), scale=128 ** -0.5, seed=3),
+    "b4h32s4096_causal": dict(B=4, H=32, S=4096, D=128, dtype="f16", mask="causal",
+                              window=(-1, -1), scale=128 ** -0.5, seed=3),
+    "b4h32s4096_win1024": dict(B=4, H=32, S=4096, D=128, dtype="f16", mask="window",
+                               window=(1024, 0), scale=128 ** -0.5, seed=3),
+    "b4h32s4096_win1000": dict(B=4, H=32, S=4096, D=128, dtype="f16", mask="window",
+                               window=(1000, 0), scale=128 ** -0.5, seed=3),
+    "long_bf16_outliers": dict(B=1, H=64, S=16384, D=128, dtype="bf16", mask="causal",
+                               window=(-1, -1), scale=128 ** -0.5, seed=5,
+                               outlier_frac=0.01, outlier_scale=20.0),
+}
+
+HEADLINE = "b4h32s4096_causal"
+
+
+def f32_to_bits(x, dtype):
+    """Round fp32 values once to ``dtype`` ('f16' or 'bf16'); return uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        u = x.view(np.uint32)
+        # round to nearest, ties to even, on the 16 discarded bits
+        bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+        return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_qkv(B, H, S, D, dtype, seed, outlier_frac=0.0, outlier_scale=20.0):
+    """Draw q, k, v per the module recipe; return three uint16 [B,H,S,D] arrays."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, S, D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if outlier_frac > 0.0 and S > 0:
+        n = int(round(outlier_frac * S))
+        for b in range(B):
+            for h in range(H):
+                if n:
+                    rows = rng.choice(S, size=n, replace=False)
+                    k[b, h, rows, :] *= np.float32(outlier_scale)
+    return f32_to_bits(q, dtype), f32_to_bits(k, dtype), f32_to_bits(v, dtype)
+
+
+def workload_inputs(name):
+    """(q, k, v) bit arrays for a named workload."""
+    w = WORKLOADS[name]
+    return make_qkv(w["B"], w["H"], w["S"], w["D"], w["dtype"], w["seed"],
+                    w.get("outlier_frac", 0.0), w.get("outlier_scale", 20.0))
+
+
+def digest(*arrays):
+    """SHA-256 over the raw bytes of the arrays (for determinism checks)."""
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()

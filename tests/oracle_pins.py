@@ -1,0 +1,337 @@
+"""Pins for the fp64 CPU oracle: checks against things other than itself.
+
+Each ``pin_*`` function takes a loaded oracle and raises AssertionError when
+the oracle disagrees with a closed form, an invariant, a special case that
+reduces to a library routine, or the pages' printed numbers. They are plain
+functions (not tests) so that the suite can also run them against copies of
+the oracle with a deliberate mistake built in and show that one of them fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from synth import f32_to_bits, make_qkv
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+MASK_CASES = [
+    ("full", (-1, -1)),
+    ("causal", (-1, -1)),
+    ("window", (3, 0)),
+    ("window", (0, 2)),
+    ("window", (5, 7)),
+    ("window", (-1, 4)),
+    ("window", (6, -1)),
+]
+
+
+def _bits(x, dtype="f16"):
+    return f32_to_bits(np.asarray(x, dtype=np.float32), dtype)
+
+
+def _decode_ref(bits, dtype):
+    """Decode with library routines (numpy's float16, torch's bfloat16)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    return t.double().numpy()
+
+
+def _bool_mask(S, mask, window):
+    """Visibility as a boolean [S, S] matrix, built with numpy index arithmetic."""
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    if mask == "full":
+        return np.ones((S, S), dtype=bool)
+    if mask == "causal":
+        return j <= i
+    wl, wr = window
+    ok = np.ones((S, S), dtype=bool)
+    if wl >= 0:
+        ok &= j >= i - wl
+    if wr >= 0:
+        ok &= j <= i + wr
+    return ok
+
+
+# --------------------------------------------------------------------------
+# encodings
+
+
+def pin_decoders(orc):
+    """Every fp16 and bf16 bit pattern decodes as numpy / torch decode it."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dtype in ("f16", "bf16"):
+        got = orc.decode(allbits, dtype)
+        ref = _decode_ref(allbits, dtype)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), dtype
+        assert np.array_equal(got[~nan], ref[~nan]), dtype
+        # signed zeros keep their sign
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), dtype
+
+
+# --------------------------------------------------------------------------
+# mask predicate and pair counts
+
+
+def _window_count_closed(S, wl, wr):
+    """Per-row count of an inclusive window, summed (no pair enumeration)."""
+    total = 0
+    for i in range(S):
+        lo = 0 if wl < 0 else max(0, i - wl)
+        hi = S - 1 if wr < 0 else min(S - 1, i + wr)
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def pin_pair_counts(orc):
+    """Pair counts: S^2, S(S+1)/2, the causal-window closed form, mirror symmetry."""
+    for S in (1, 2, 3, 63, 64, 65, 127, 128, 129, 300):
+        assert orc.pair_count(S, "full") == S * S
+        assert orc.pair_count(S, "causal") == S * (S + 1) // 2
+        assert orc.pair_count(S, "window", (-1, -1)) == S * S
+        assert orc.pair_count(S, "window", (-1, 0)) == S * (S + 1) // 2
+        for wl in (0, 1, 63, 64, 65, S - 1):
+            if 0 <= wl < S:
+                closed = wl * (wl + 1) // 2 + (S - wl) * (wl + 1)
+                assert orc.pair_count(S, "window", (wl, 0)) == closed, (S, wl)
+        for wl in (-1, 0, 1, 5, 64, S, S + 5):
+            for wr in (-1, 0, 2, 65, S + 1):
+                c = orc.pair_count(S, "window", (wl, wr))
+                assert c == _window_count_closed(S, wl, wr), (S, wl, wr)
+                # reversing the sequence swaps the two window sides
+                assert c == orc.pair_count(S, "window", (wr, wl)), (S, wl, wr)
+
+
+def pin_page_numbers(orc):
+    """Numbers the pages print (tests/golden/page_numbers.json)."""
+    with open(os.path.join(GOLDEN, "page_numbers.json")) as f:
+        items = json.load(f)
+    by_key = {it["key"]: it for it in items}
+    n = orc.pair_count(4096, "full")
+    assert n == by_key["full_scores_s4096"]["value"]
+    assert n * 4 == by_key["fp32_score_bytes_s4096"]["value"]
+    assert 1.0 / math.sqrt(64) == by_key["scale_d64"]["value"]
+
+
+# --------------------------------------------------------------------------
+# attention values
+
+
+def pin_sdpa(orc):
+    """Matches torch's CPU fp64 scaled_dot_product_attention with a boolean mask,
+    and torch.logsumexp of the masked scaled scores for the LSE."""
+    rng = np.random.default_rng(11)
+    for dtype in ("f16", "bf16"):
+        for (S, D) in ((1, 8), (5, 8), (37, 16), (64, 64), (100, 32)):
+            q, k, v = make_qkv(2, 2, S, D, dtype, seed=int(rng.integers(1 << 30)))
+            qd = torch.from_numpy(_decode_ref(q, dtype))
+            kd = torch.from_numpy(_decode_ref(k, dtype))
+            vd = torch.from_numpy(_decode_ref(v, dtype))
+            for mask, window in MASK_CASES:
+                scale = 1.0 / math.sqrt(D) if mask != "window" else 0.3
+                bm = torch.from_numpy(_bool_mask(S, mask, window))
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qd, kd, vd, attn_mask=bm, scale=scale).numpy()
+                scores = torch.matmul(qd, kd.transpose(-1, -2)) * scale
+                scores = scores.masked_fill(~bm, float("-inf"))
+                lse_ref = torch.logsumexp(scores, dim=-1).numpy()
+                o, lse = orc.attention(q, k, v, dtype, scale, mask, window)
+                assert np.max(np.abs(o - ref)) < 1e-12, (dtype, S, D, mask, window)
+                assert np.max(np.abs(lse - lse_ref)) < 1e-12, (dtype, S, D, mask, window)
+
+
+def pin_uniform_weights(orc):
+    """Q = 0 makes every visible key weigh the same: O_i is the mean of the
+    visible V rows (prefix means for causal) and LSE_i = ln(count_i)."""
+    S, D = 50, 16
+    _, _, v = make_qkv(1, 1, S, D, "f16", seed=5)
+    q = np.zeros_like(v)
+    _, k, _ = make_qkv(1, 1, S, D, "f16", seed=6)
+    vd = _decode_ref(v, "f16")[0, 0]
+    for mask, window in MASK_CASES + [("window", (10, 0))]:
+        vis = _bool_mask(S, mask, window)
+        cnt = vis.sum(axis=1)
+        means = (vis.astype(np.float64) @ vd) / cnt[:, None]
+        if mask == "causal":
+            prefix = np.cumsum(vd, axis=0) / np.arange(1, S + 1)[:, None]
+            assert np.max(np.abs(means - prefix)) < 1e-12
+        o, lse = orc.attention(q, k, v, "f16", 0.7, mask, window)
+        assert np.max(np.abs(o[0, 0] - means)) < 1e-12, (mask, window)
+        assert np.max(np.abs(lse[0, 0] - np.log(cnt))) < 1e-12, (mask, window)
+    # scale = 0 with nonzero Q is the same case
+    qn, _, _ = make_qkv(1, 1, S, D, "f16", seed=7)
+    o0, lse0 = orc.attention(qn, k, v, "f16", 0.0, "causal")
+    prefix = np.cumsum(vd, axis=0) / np.arange(1, S + 1)[:, None]
+    assert np.max(np.abs(o0[0, 0] - prefix)) < 1e-12
+    assert np.max(np.abs(lse0[0, 0] - np.log(np.arange(1, S + 1)))) < 1e-12
+
+
+def pin_constant_v(orc):
+    """V rows all equal to one vector c give O_i = c for every row and mask."""
+    S, D = 40, 8
+    q, k, _ = make_qkv(1, 2, S, D, "f16", seed=8)
+    c = np.array([1.5, -2.0, 0.25, 3.0, 0.0, -0.5, 7.0, 1.0], dtype=np.float32)
+    v = _bits(np.broadcast_to(c, (1, 2, S, D)))
+    for mask, window in MASK_CASES:
+        o, _ = orc.attention(q, k, v, "f16", 0.35, mask, window)
+        assert np.max(np.abs(o - c.astype(np.float64))) < 1e-14, (mask, window)
+
+
+def pin_single_visible_key(orc):
+    """Causal row 0 sees only key 0: O_0 = V_0 exactly, LSE_0 = scale*q_0.k_0."""
+    S, D = 9, 16
+    q, k, v = make_qkv(1, 1, S, D, "f16", seed=9)
+    scale = 0.25
+    o, lse = orc.attention(q, k, v, "f16", scale, "causal")
+    qd, kd, vd = (_decode_ref(x, "f16")[0, 0] for x in (q, k, v))
+    assert np.array_equal(o[0, 0, 0], vd[0])
+    assert abs(lse[0, 0, 0] - scale * float(np.dot(qd[0], kd[0]))) < 1e-12
+    # window (0, 0) sees only the key at the same position: O_i = V_i
+    o, _ = orc.attention(q, k, v, "f16", scale, "window", (0, 0))
+    assert np.array_equal(o[0, 0], vd)
+
+
+def pin_one_hot_dominant(orc):
+    """One visible key scoring 64 above every other copies that key's V row."""
+    S, D = 12, 16
+    target = [0, 0, 1, 3, 2, 5, 6, 0, 8, 4, 10, 11]   # target[i] <= i: causal-visible
+    K = np.zeros((S, D), np.float32)
+    Q = np.zeros((S, D), np.float32)
+    for j in range(S):
+        K[j, j] = 8.0
+    for i in range(S):
+        Q[i, target[i]] = 8.0
+    _, _, v = make_qkv(1, 1, S, D, "f16", seed=10)
+    q = _bits(Q[None, None])
+    k = _bits(K[None, None])
+    vd = _decode_ref(v, "f16")[0, 0]
+    for mask in ("causal", "full"):
+        o, lse = orc.attention(q, k, v, "f16", 1.0, mask)
+        for i in range(S):
+            nvis = (i + 1) if mask == "causal" else S
+            assert np.max(np.abs(o[0, 0, i] - vd[target[i]])) <= 1e-15, (mask, i)
+            expect = 64.0 + math.log1p((nvis - 1) * math.exp(-64.0))
+            assert abs(lse[0, 0, i] - expect) < 1e-12, (mask, i)
+
+
+def pin_two_keys(orc):
+    """S = 2, full mask: O_0 = sigmoid(s00 - s01) V_0 + sigmoid(s01 - s00) V_1."""
+    D = 8
+    q, k, v = make_qkv(1, 1, 2, D, "f16", seed=12)
+    qd, kd, vd = (_decode_ref(x, "f16")[0, 0] for x in (q, k, v))
+    scale = 0.9
+    o, lse = orc.attention(q, k, v, "f16", scale, "full")
+    for i in range(2):
+        s0 = scale * float(np.dot(qd[i], kd[0]))
+        s1 = scale * float(np.dot(qd[i], kd[1]))
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+        assert np.max(np.abs(o[0, 0, i] - (w0 * vd[0] + w1 * vd[1]))) < 1e-14
+        assert abs(lse[0, 0, i] - np.logaddexp(s0, s1)) < 1e-13
+
+
+def pin_shift_invariance(orc):
+    """Adding one vector u to every key row leaves O unchanged and shifts
+    LSE_i by scale*q_i.u (exactly representable integer-valued inputs)."""
+    rng = np.random.default_rng(13)
+    S, D = 30, 8
+    Q = rng.integers(-3, 4, size=(1, 1, S, D)).astype(np.float32)
+    K = rng.integers(-3, 4, size=(1, 1, S, D)).astype(np.float32)
+    u = rng.integers(-2, 3, size=D).astype(np.float32)
+    _, _, v = make_qkv(1, 1, S, D, "f16", seed=14)
+    scale = 0.125
+    for mask, window in MASK_CASES:
+        o1, l1 = orc.attention(_bits(Q), _bits(K), v, "f16", scale, mask, window)
+        o2, l2 = orc.attention(_bits(Q), _bits(K + u), v, "f16", scale, mask, window)
+        shift = scale * (Q[0, 0].astype(np.float64) @ u.astype(np.float64))
+        assert np.max(np.abs(o1 - o2)) < 1e-12, (mask, window)
+        assert np.max(np.abs((l2 - l1)[0, 0] - shift)) < 1e-12, (mask, window)
+
+
+def pin_permutation(orc):
+    """Full mask: permuting the (K, V) rows together changes nothing."""
+    S, D = 33, 16
+    q, k, v = make_qkv(1, 2, S, D, "bf16", seed=15)
+    perm = np.random.default_rng(16).permutation(S)
+    o1, l1 = orc.attention(q, k, v, "bf16", 0.2, "full")
+    o2, l2 = orc.attention(q, k[:, :, perm], v[:, :, perm], "bf16", 0.2, "full")
+    assert np.max(np.abs(o1 - o2)) < 1e-13
+    assert np.max(np.abs(l1 - l2)) < 1e-13
+
+
+def pin_linearity_in_v(orc):
+    """O(2 V1 - V2) = 2 O(V1) - O(V2) (integer-valued V, exact in fp16)."""
+    rng = np.random.default_rng(17)
+    S, D = 26, 8
+    q, k, _ = make_qkv(1, 1, S, D, "f16", seed=18)
+    V1 = rng.integers(-8, 9, size=(1, 1, S, D)).astype(np.float32)
+    V2 = rng.integers(-8, 9, size=(1, 1, S, D)).astype(np.float32)
+    for mask, window in MASK_CASES:
+        a, _ = orc.attention(q, k, _bits(V1), "f16", 0.3, mask, window)
+        b, _ = orc.attention(q, k, _bits(V2), "f16", 0.3, mask, window)
+        c, _ = orc.attention(q, k, _bits(2 * V1 - V2), "f16", 0.3, mask, window)
+        assert np.max(np.abs(c - (2 * a - b))) < 1e-12, (mask, window)
+
+
+def pin_mask_equivalences(orc):
+    """window(-1,-1) = full, window(-1,0) = causal, window(S-1,0) = causal,
+    window(S-1,S-1) = full, bit for bit."""
+    S, D = 45, 16
+    q, k, v = make_qkv(2, 1, S, D, "f16", seed=19)
+    full = orc.attention(q, k, v, "f16", 0.25, "full")
+    causal = orc.attention(q, k, v, "f16", 0.25, "causal")
+    for window, ref in (((-1, -1), full), ((-1, 0), causal), ((S - 1, 0), causal),
+                        ((S - 1, S - 1), full), ((S + 3, -1), full)):
+        got = orc.attention(q, k, v, "f16", 0.25, "window", window)
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), window
+
+
+def pin_probabilities(orc):
+    """The materialised probability rows sum to 1, vanish where masked, and
+    P @ V (numpy) reproduces O."""
+    S, D = 24, 8
+    q, k, v = make_qkv(1, 1, S, D, "f16", seed=20)
+    vd = _decode_ref(v, "f16")[0, 0]
+    for mask, window in MASK_CASES:
+        p, o, _ = orc.attention_probs(q[0, 0], k[0, 0], v[0, 0], "f16", 0.5, mask, window)
+        vis = _bool_mask(S, mask, window)
+        assert np.all(p[~vis] == 0.0), (mask, window)
+        assert np.all(p[vis] > 0.0), (mask, window)
+        assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-14, (mask, window)
+        assert np.max(np.abs(p @ vd - o)) < 1e-13, (mask, window)
+
+
+def pin_scale_is_a_multiplier(orc):
+    """Doubling the scale equals doubling Q (exact in fp16)."""
+    S, D = 20, 8
+    rng = np.random.default_rng(21)
+    Q = rng.integers(-4, 5, size=(1, 1, S, D)).astype(np.float32)
+    _, k, v = make_qkv(1, 1, S, D, "f16", seed=22)
+    a = orc.attention(_bits(Q), k, v, "f16", 0.25, "causal")
+    b = orc.attention(_bits(2 * Q), k, v, "f16", 0.125, "causal")
+    assert np.max(np.abs(a[0] - b[0])) < 1e-12 and np.max(np.abs(a[1] - b[1])) < 1e-12
+
+
+ALL_PINS = [
+    pin_decoders,
+    pin_pair_counts,
+    pin_page_numbers,
+    pin_sdpa,
+    pin_uniform_weights,
+    pin_constant_v,
+    pin_single_visible_key,
+    pin_one_hot_dominant,
+    pin_two_keys,
+    pin_shift_invariance,
+    pin_permutation,
+    pin_linearity_in_v,
+    pin_mask_equivalences,
+    pin_probabilities,
+    pin_scale_is_a_multiplier,
+]

@@ -1,0 +1,28 @@
+"""Each deliberate mistake built into a copy of the oracle fails at least one
+pin, so the pins are sensitive to the mistakes they are meant to catch.
+
+Planted mistakes (see ORACLE_PLANT in oracle/attn_oracle.c):
+  1 scale dropped, 2 causal diagonal dropped, 3 window left edge exclusive,
+  4 score sign flipped, 5 wrong V row, 6 log base 2 in the LSE.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("plant", [1, 2, 3, 4, 5, 6])
+def test_planted_mistake_is_caught(plant):
+    bad = oracle.load_planted(plant)
+    try:
+        caught = []
+        for pin in ALL_PINS:
+            try:
+                pin(bad)
+            except AssertionError:
+                caught.append(pin.__name__)
+        assert caught, f"no pin caught planted mistake {plant}"
+    finally:
+        os.remove(bad.path)
