@@ -1,0 +1,220 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one fa_fwd call over the whole workload (default: B=4, H=32,
+S=4096, D=128, fp16, causal, scale 1/sqrt(128)), inputs resident in HBM.
+Prints one JSON line: TFLOP/s (4*D*B*H*visible pairs per call / average
+kernel time), the roofline of the kernel against the dense fp16 MFMA peak,
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds T]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X dense fp16/bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
+PEAK_FP16_TFLOPS = 2516.6
+KERNEL_SOURCES = ["tiled_attention_11_amd/csrc/fa_kernel.hip",
+                  "tiled_attention_11_amd/csrc/fa_internal.h"]
+
+
+def kernel_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}.pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sha256():
+        return None
+    return int(val.group(1))
+
+
+def visible_per_row(S, mask, window, rows_i):
+    """Visible keys of each query position (for FLOP accounting)."""
+    import numpy as np
+    i = np.asarray(rows_i, dtype=np.int64)
+    if mask == "full":
+        lo, hi = np.zeros_like(i), np.full_like(i, S - 1)
+    elif mask == "causal":
+        lo, hi = np.zeros_like(i), i
+    else:
+        wl, wr = window
+        lo = np.maximum(0, i - wl) if wl >= 0 else np.zeros_like(i)
+        hi = np.minimum(S - 1, i + wr) if wr >= 0 else np.full_like(i, S - 1)
+    return np.maximum(0, hi - lo + 1)
+
+
+def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, seconds):
+    """Time the fp64 oracle on a bounded random sample of the workload's rows;
+    also report how those rows compare with the GPU output."""
+    import numpy as np
+
+    import oracle
+    from tests.parity import compare
+
+    orc = oracle.load()
+    B, H, S, D = w["B"], w["H"], w["S"], w["D"]
+    total = B * H * S
+    rng = np.random.default_rng(1234)
+    args = (q, k, v, w["dtype"], w["scale"], w["mask"], w["window"])
+    probe = rng.choice(total, size=min(64, total), replace=False)
+    t0 = time.perf_counter()
+    orc.attention_rows(*args, rows=probe)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    n = int(min(total, max(64, len(probe) * seconds / dt)))
+    rows = np.sort(rng.choice(total, size=n, replace=False))
+    t0 = time.perf_counter()
+    o_ref, lse_ref = orc.attention_rows(*args, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = int(visible_per_row(S, w["mask"], w["window"], rows % S).sum())
+    flops = 4 * D * pairs
+    st = compare(o_gpu.reshape(-1, D)[rows], lse_gpu.reshape(-1)[rows], o_ref, lse_ref,
+                 w["dtype"])
+    base = {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.max_threads(),
+        "kind": "oracle",
+        "sample": (f"{n} query rows drawn uniformly (seed 1234) from the same workload, "
+                   f"{pairs} visible pairs, {dt:.2f} s wall, fp64"),
+    }
+    parity = {"rows": n, "pass": st["pass"], "max_abs": st["max_abs"],
+              "mean_abs": st["mean_abs"], "lse_max_abs": st.get("lse_max_abs")}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU oracle sample (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(reference kernel for rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(attention heads shard across GPUs with no communication; run one "
+              "process per GPU on its own heads).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import tiled_attention_11_amd as fa
+
+    name = args.workload or synth.HEADLINE
+    w = synth.WORKLOADS[name]
+    B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
+    wl, wr = w["window"]
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    q, k, v = synth.workload_inputs(name)
+    tq, tk, tv = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
+    out = torch.empty_like(tq)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+
+    def step():
+        fa.forward(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
+                   lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_wall = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]) * 1e-3
+    total_s = evs[0].elapsed_time(evs[-1]) * 1e-3
+    avg_s = total_s / args.steps
+    print(f"[bench] timed {args.steps} steps: avg {avg_s * 1e6:.1f} us, median "
+          f"{np.median(per) * 1e6:.1f} us, wall {t_wall:.3f} s", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flops = fa.fa_fwd_flops(B, H, S, D, fa._mask_code(w["mask"]), wl, wr)
+    tflops = flops / avg_s / 1e12
+    traffic = counted_traffic(name)
+
+    result = {
+        "metric": "attention fwd TFLOP/s and % of fp16 MFMA peak, B4 H32 S4096 D128 causal",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(avg_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if dtype == "f16" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{name}: B={B} H={H} S={S} D={D} {dtype} {w['mask']}"
+                         + (f" window=({wl},{wr})" if w["mask"] == "window" else "")
+                         + f" scale={w['scale']:.6g}"),
+            "B": B, "H": H, "S": S, "D": D, "mask": w["mask"], "window": [wl, wr],
+            "flops_per_step": flops,
+        },
+        "pct_of_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 2),
+        "median_launch_us": round(float(np.median(per)) * 1e6, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        torch.cuda.synchronize()
+        o_bits = out.cpu().view(torch.int16).numpy().view(np.uint16)
+        base, parity = cpu_baseline(w, q, k, v, o_bits, lse.cpu().numpy(), args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity_sample"] = parity
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,122 @@
+/*
+ * fa.h -- C ABI of the fused attention forward on AMD Instinct MI355X (gfx950).
+ *
+ * Computes, for every batch b, head h and query row i,
+ *     O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:] + mask_ij) V[b,h,j,:]
+ * tile by tile: a block of Q rows stays on chip while K/V column blocks stream
+ * through LDS; a running row maximum and row sum (online softmax) rescale an
+ * fp32 output accumulator, so the S x S score matrix never reaches memory.
+ *
+ * Defining passages:
+ *   - the operation: Ascend C FlashAttention-2 tile-fusion page
+ *     (ascendai.csdn.net), sections 1.1 and 1.2 (O_i = sum_j e^(P_ij - m_i) V_j
+ *     / sum_j e^(P_ij - m_i), with m_i the row maximum); "FlashAttention on
+ *     Ascend NPU: from principle to practice" (hwcomputing.csdn.net,
+ *     6a0fe629), section "core idea: IO-aware" (scale 1/sqrt(head_dim) on QK^T);
+ *   - the [B,H,S,D] fp16 tensors, causal flag and explicit scale:
+ *     ops-transformer FlashAttention walkthrough (hwcomputing.csdn.net,
+ *     6a0ef689), section on the complete operator (aclnn call example);
+ *   - full / causal / (window_left, window_right) masks: catlass FlashAttention
+ *     article (lnwmold.com/news/1200460), section "usage";
+ *   - fp32 softmax and accumulation with fp16 inputs and output: the
+ *     ops-transformer walkthrough, pitfall 3, and the tile-fusion page,
+ *     section 10 (best practice).
+ *
+ * All functions are reentrant and thread-safe; the library keeps no state.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Mask modes.
+ *   FA_MASK_FULL   every key is visible (win_l, win_r ignored);
+ *   FA_MASK_CAUSAL key j is visible from query i iff j <= i (win_l, win_r ignored);
+ *   FA_MASK_WINDOW key j is visible iff i - win_l <= j <= i + win_r, both ends
+ *                  inclusive; a negative win_l (win_r) leaves the left (right)
+ *                  side unbounded, so (-1, 0) is causal and (-1, -1) is full. */
+typedef enum {
+    FA_MASK_FULL = 0,
+    FA_MASK_CAUSAL = 1,
+    FA_MASK_WINDOW = 2
+} fa_mask_mode;
+
+/* Element type of q, k, v and o. */
+typedef enum {
+    FA_DTYPE_FP16 = 0, /* IEEE binary16 */
+    FA_DTYPE_BF16 = 1  /* bfloat16 */
+} fa_dtype;
+
+/* Return codes. Every code except FA_ERR_HIP is returned before anything is
+ * enqueued or written. */
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum, non-finite
+                                scale, output overlapping an input */
+    FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64 or 128 */
+    FA_ERR_ALIGNMENT = -3,   /* q/k/v/o not 16-byte aligned, lse not 4-byte aligned */
+    FA_ERR_TOO_LARGE = -4,   /* a head's [S, D] block is 2^31 bytes or more, or the
+                                launch grid or FLOP count would overflow */
+    FA_ERR_HIP = -5          /* the HIP runtime rejected the kernel launch */
+} fa_status;
+
+/*
+ * fa_fwd -- attention forward, O = softmax(scale * Q K^T + mask) V.
+ *
+ * q, k, v  device pointers, contiguous row-major [B, H, S, D] (D fastest), element
+ *          type `dtype`; read only.
+ * o        device pointer, [B, H, S, D] of `dtype`; fully overwritten. Each value
+ *          is the fp32 result rounded to nearest even.
+ * lse      device pointer to fp32 [B, H, S], or NULL to skip it; fully
+ *          overwritten with the natural-log log-sum-exp of each row's visible
+ *          scaled scores, log(sum_j exp(scale * q_i . k_j)).
+ * B, H, S  batch, heads, sequence length (>= 0). If B*H*S == 0 the call does
+ *          nothing and returns FA_OK without reading any pointer.
+ * D        head dimension: 64 or 128.
+ * scale    finite multiplier of Q K^T (1/sqrt(D) is the usual choice); any sign.
+ * mask_mode, win_l, win_r  see fa_mask_mode.
+ * dtype    fa_dtype of q, k, v and o.
+ * stream   HIP stream on the current device; the call only enqueues work
+ *          (asynchronous) and device faults surface at the caller's next
+ *          synchronisation.
+ *
+ * Ownership: the caller owns every buffer; the library allocates nothing,
+ * needs no workspace and keeps no reference after return. o and lse must not
+ * overlap q, k, v or each other (checked on the host).
+ * Arithmetic: QK^T and PV run on fp16/bf16 matrix cores with fp32 accumulation;
+ * softmax state is fp32; probabilities are rounded to `dtype` before PV and
+ * the row sum uses the unrounded fp32 values. Results are bitwise
+ * deterministic for a given input, device and library build.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int S, int D, float scale, int mask_mode, int win_l,
+           int win_r, int dtype, hipStream_t stream);
+
+/*
+ * fa_visible_pairs -- number of (query, key) pairs of one S x S head that the
+ * mask leaves visible (S >= 0). Returns the count, or a negative fa_status.
+ */
+int64_t fa_visible_pairs(int S, int mask_mode, int win_l, int win_r);
+
+/*
+ * fa_fwd_flops -- the algorithmic FLOPs of one fa_fwd call: 4 * D * B * H *
+ * fa_visible_pairs(S, ...), counting a multiply-add as 2 FLOPs for each of the
+ * two products QK^T and PV over visible pairs only. Returns the count, or a
+ * negative fa_status.
+ */
+int64_t fa_fwd_flops(int B, int H, int S, int D, int mask_mode, int win_l, int win_r);
+
+/* fa_strerror -- static description of a status code (never NULL). */
+const char *fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

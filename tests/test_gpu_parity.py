@@ -1,0 +1,205 @@
+"""The HIP path against the fp64 oracle, through the C ABI (needs a gfx950 GPU).
+
+Every case prints its name, shape and seed before touching the GPU."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+import tiled_attention_11_amd as fa
+from parity import compare, decode, sample_rows, to_bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_run(q, k, v, dtype, scale, mask, window=(-1, -1), with_lse=True):
+    tq, tk, tv = (to_device(x, dtype) for x in (q, k, v))
+    o, lse = fa.forward(tq, tk, tv, scale=scale, mask=mask, window=window,
+                        return_lse=with_lse)
+    torch.cuda.synchronize()
+    return to_bits(o), (lse.cpu().numpy() if lse is not None else None)
+
+
+def check_full(orc, q, k, v, dtype, scale, mask, window=(-1, -1)):
+    o_bits, lse = gpu_run(q, k, v, dtype, scale, mask, window)
+    o_ref, lse_ref = orc.attention(q, k, v, dtype, scale, mask, window)
+    st = compare(o_bits, lse, o_ref, lse_ref, dtype)
+    assert st["pass"], st
+    return st
+
+
+# ---------------------------------------------------------------------------
+# whole-tensor parity at sizes spanning several tiles and a ragged tail
+
+SHAPES = [(2, 3, 1000, 128), (1, 4, 777, 64), (2, 2, 320, 128), (1, 2, 300, 64)]
+MASKS = [("full", (-1, -1)), ("causal", (-1, -1)), ("window", (100, 0)),
+         ("window", (37, 50)), ("window", (-1, 20)), ("window", (300, -1)),
+         ("window", (64, 64))]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("mask,window", MASKS, ids=lambda m: str(m))
+def test_parity_whole_tensor(orc, dtype, shape, mask, window):
+    B, H, S, D = shape
+    seed = 100 + S + D
+    say("whole", dtype, shape, mask, window, "seed", seed)
+    q, k, v = synth.make_qkv(B, H, S, D, dtype, seed)
+    check_full(orc, q, k, v, dtype, 1.0 / math.sqrt(D), mask, window)
+
+
+@pytest.mark.parametrize("S", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask,window", [("causal", (-1, -1)), ("full", (-1, -1)),
+                                         ("window", (40, 3))], ids=str)
+def test_parity_tails(orc, S, D, mask, window):
+    say("tail", S, D, mask, window)
+    q, k, v = synth.make_qkv(1, 2, S, D, "f16", seed=7 + S)
+    check_full(orc, q, k, v, "f16", 1.0 / math.sqrt(D), mask, window)
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size, on sampled rows
+
+_CACHE = {}
+
+
+def _inputs(name):
+    w = synth.WORKLOADS[name]
+    key = (w["B"], w["H"], w["S"], w["D"], w["dtype"], w["seed"], w.get("outlier_frac", 0.0))
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = synth.workload_inputs(name)
+    return _CACHE[key]
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_parity_workload(orc, name):
+    w = synth.WORKLOADS[name]
+    B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
+    say("workload", name, (B, H, S, D), dtype, w["mask"], w["window"], "seed", w["seed"])
+    q, k, v = _inputs(name)
+    o_bits, lse = gpu_run(q, k, v, dtype, w["scale"], w["mask"], w["window"])
+    wl = w["window"][0]
+    extra = (wl - 1, wl, wl + 1, wl + 63, wl + 64) if wl > 0 else ()
+    rows = sample_rows(B, H, S, 1024 if B * H * S > 65536 else B * H * S, seed=w["seed"],
+                       extra_i=extra)
+    o_ref, lse_ref = orc.attention_rows(q, k, v, dtype, w["scale"], w["mask"], w["window"], rows)
+    st = compare(o_bits.reshape(-1, D)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, dtype)
+    say("stats", st)
+    assert st["pass"], st
+
+
+# ---------------------------------------------------------------------------
+# closed forms through the GPU path
+
+def test_zero_q_gives_prefix_means(orc):
+    S, D = 333, 128
+    _, k, v = synth.make_qkv(1, 1, S, D, "f16", seed=31)
+    q = np.zeros_like(k)
+    say("zero-q prefix means", S, D)
+    o_bits, lse = gpu_run(q, k, v, "f16", 0.088, "causal")
+    vd = decode(v, "f16")[0, 0]
+    prefix = np.cumsum(vd, axis=0) / np.arange(1, S + 1)[:, None]
+    o = decode(o_bits, "f16")[0, 0]
+    assert np.max(np.abs(o - prefix)) < 2e-3
+    assert np.max(np.abs(lse[0, 0] - np.log(np.arange(1, S + 1)))) < 1e-5
+
+
+def test_constant_v_is_reproduced():
+    S, D = 257, 64
+    q, k, _ = synth.make_qkv(2, 2, S, D, "bf16", seed=32)
+    c = (np.arange(D) % 7 - 3).astype(np.float32) * 0.5
+    v = synth.f32_to_bits(np.broadcast_to(c, (2, 2, S, D)), "bf16")
+    for mask, window in MASKS:
+        say("constant v", mask, window)
+        o_bits, _ = gpu_run(q, k, v, "bf16", 0.125, mask, window)
+        o = decode(o_bits, "bf16")
+        assert np.max(np.abs(o - c)) <= 2 ** -7, (mask, window)
+
+
+def test_one_hot_dominant_key_copies_v_row():
+    S, D = 128, 128
+    target = np.array([max(0, i - (i * 7) % 11) for i in range(S)])   # target <= i
+    Q = np.zeros((1, 1, S, D), np.float32)
+    K = np.zeros((1, 1, S, D), np.float32)
+    for j in range(S):
+        K[0, 0, j, j % D] = 8.0
+    for i in range(S):
+        Q[0, 0, i, target[i] % D] = 8.0
+    _, _, v = synth.make_qkv(1, 1, S, D, "f16", seed=33)
+    say("one-hot dominant key")
+    o_bits, _ = gpu_run(synth.f32_to_bits(Q, "f16"), synth.f32_to_bits(K, "f16"), v, "f16", 1.0,
+                        "causal")
+    o = decode(o_bits, "f16")[0, 0]
+    vd = decode(v, "f16")[0, 0]
+    assert np.max(np.abs(o - vd[target])) <= 2e-3
+
+
+# ---------------------------------------------------------------------------
+# properties of the launch
+
+def test_deterministic_bitwise():
+    q, k, v = synth.make_qkv(2, 8, 1500, 128, "f16", seed=41)
+    say("determinism")
+    a = gpu_run(q, k, v, "f16", 0.09, "causal")
+    b = gpu_run(q, k, v, "f16", 0.09, "causal")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_heads_are_independent():
+    B, H, S, D = 2, 8, 600, 64
+    q, k, v = synth.make_qkv(B, H, S, D, "bf16", seed=42)
+    say("slice independence")
+    o_all, l_all = gpu_run(q, k, v, "bf16", 0.125, "window", (200, 10))
+    for b, h in ((0, 0), (1, 5), (1, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o1, l1 = gpu_run(q[sl], k[sl], v[sl], "bf16", 0.125, "window", (200, 10))
+        assert np.array_equal(o1[0, 0], o_all[b, h]) and np.array_equal(l1[0, 0], l_all[b, h])
+
+
+def test_lse_pointer_may_be_null(orc):
+    q, k, v = synth.make_qkv(1, 2, 300, 128, "f16", seed=43)
+    say("null lse")
+    o_bits, lse = gpu_run(q, k, v, "f16", 0.1, "causal", with_lse=False)
+    assert lse is None
+    o_ref, _ = orc.attention(q, k, v, "f16", 0.1, "causal")
+    st = compare(o_bits, None, o_ref, None, "f16")
+    assert st["pass"], st
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, 0.5])
+def test_scale_sign_and_zero(orc, scale):
+    q, k, v = synth.make_qkv(1, 2, 200, 64, "f16", seed=44)
+    say("scale", scale)
+    check_full(orc, q, k, v, "f16", scale, "window", (50, 5))
+
+
+def test_empty_problems_do_nothing():
+    say("empty")
+    for shape in ((0, 2, 64, 64), (1, 0, 64, 64), (1, 2, 0, 64)):
+        t = torch.zeros(shape, dtype=torch.float16, device="cuda")
+        o, lse = fa.forward(t, t, t, mask="causal")
+        torch.cuda.synchronize()
+        assert o.shape == shape and lse.shape == shape[:3]
+
+
+def test_runs_on_a_side_stream(orc):
+    q, k, v = synth.make_qkv(1, 2, 500, 128, "bf16", seed=45)
+    say("side stream")
+    tq, tk, tv = (to_device(x, "bf16") for x in (q, k, v))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa.forward(tq, tk, tv, scale=0.1, mask="causal")
+    s.synchronize()
+    o_ref, lse_ref = orc.attention(q, k, v, "bf16", 0.1, "causal")
+    st = compare(to_bits(o), lse.cpu().numpy(), o_ref, lse_ref, "bf16")
+    assert st["pass"], st

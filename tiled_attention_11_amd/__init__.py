@@ -1,0 +1,139 @@
+"""Fused attention forward for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
+``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops`` and ``fa_strerror`` carry
+the C names and arguments (marshalling only). ``forward`` is the convenience
+entry for torch tensors: torch supplies device memory and the stream; every
+step of the computation runs in the library's HIP kernels. There is no
+fallback: if the library is missing, importing this package raises.
+"""
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
+    "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
+    "fa_strerror", "forward", "lib_path", "library",
+]
+
+FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_WINDOW = 0, 1, 2
+FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1
+_MASKS = {"full": FA_MASK_FULL, "causal": FA_MASK_CAUSAL, "window": FA_MASK_WINDOW}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path():
+    return os.environ.get("FA_LIBRARY", os.path.join(_HERE, "libfa.so"))
+
+
+def _load():
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m tiled_attention_11_amd._build` "
+            "(hipcc, gfx950) first. There is no non-HIP fallback.")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci,
+                           ci, vp]
+    lib.fa_fwd.restype = ci
+    lib.fa_visible_pairs.argtypes = [ci, ci, ci, ci]
+    lib.fa_visible_pairs.restype = ctypes.c_int64
+    lib.fa_fwd_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.fa_fwd_flops.restype = ctypes.c_int64
+    lib.fa_strerror.argtypes = [ci]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    """The loaded ``ctypes.CDLL``."""
+    return _lib
+
+
+class FaError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(f"fa_fwd failed: {fa_strerror(status)} (status {status})")
+
+
+# ---- the C functions, same names and arguments ------------------------------
+
+def fa_fwd(q, k, v, o, lse, B, H, S, D, scale, mask_mode, win_l, win_r, dtype, stream):
+    """Call ``fa_fwd`` with raw device addresses (ints); return its status."""
+    return _lib.fa_fwd(q, k, v, o, lse, B, H, S, D, scale, mask_mode, win_l, win_r, dtype,
+                       stream)
+
+
+def fa_visible_pairs(S, mask_mode, win_l=-1, win_r=-1):
+    return _lib.fa_visible_pairs(S, mask_mode, win_l, win_r)
+
+
+def fa_fwd_flops(B, H, S, D, mask_mode, win_l=-1, win_r=-1):
+    return _lib.fa_fwd_flops(B, H, S, D, mask_mode, win_l, win_r)
+
+
+def fa_strerror(status):
+    return _lib.fa_strerror(status).decode()
+
+
+# ---- torch convenience ---------------------------------------------------------
+
+def _mask_code(mask):
+    if isinstance(mask, int):
+        return mask
+    try:
+        return _MASKS[mask]
+    except KeyError:
+        raise ValueError(f"mask must be one of {sorted(_MASKS)}, got {mask!r}") from None
+
+
+def forward(q, k, v, *, scale=None, mask="full", window=(-1, -1), out=None, lse=None,
+            return_lse=True, stream=None):
+    """Attention forward on torch device tensors.
+
+    q, k, v: contiguous [B, H, S, D] float16 or bfloat16 tensors on one GPU.
+    scale: defaults to 1/sqrt(D). mask: "full", "causal" or "window" with
+    ``window=(win_l, win_r)`` (inclusive; negative = unbounded side).
+    out / lse: optional preallocated outputs. Returns ``(o, lse)`` (``lse`` is
+    None when ``return_lse`` is False and no buffer is given).
+    """
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor on q's device")
+    wl, wr = window
+    dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        status = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr() if lse is not None else None, B, H, S, D,
+                        float(scale), _mask_code(mask), int(wl), int(wr), dtype, stream)
+    if status != 0:
+        raise FaError(status)
+    return out, lse

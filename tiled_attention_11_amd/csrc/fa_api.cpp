@@ -1,0 +1,142 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation, the
+// visible-pair and FLOP counts, and the hand-off to the gfx950 kernels.
+//
+// Validation is plain host code and runs before any HIP call, so every error
+// except FA_ERR_HIP leaves nothing enqueued and nothing written.
+
+#include "fa.h"
+#include "fa_internal.h"
+
+#include <cmath>
+#include <cstdint>
+
+namespace {
+
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+// Visible key range [lo, hi] of query row i (an empty range has lo > hi), from
+// the window form of the mask that fa_internal.h describes.
+inline void key_range(int64_t i, int64_t S, int64_t win_lo, int64_t win_hi,
+                      int64_t *lo, int64_t *hi) {
+    int64_t a = i - win_lo, b = i + win_hi;
+    *lo = a > 0 ? a : 0;
+    *hi = b < S - 1 ? b : S - 1;
+}
+
+// Mask mode and window arguments -> (win_lo, win_hi); false on a bad mode.
+bool window_of(int mask_mode, int win_l, int win_r, int *win_lo, int *win_hi) {
+    switch (mask_mode) {
+    case FA_MASK_FULL:
+        *win_lo = fa::kUnbounded;
+        *win_hi = fa::kUnbounded;
+        return true;
+    case FA_MASK_CAUSAL:
+        *win_lo = fa::kUnbounded;
+        *win_hi = 0;
+        return true;
+    case FA_MASK_WINDOW:
+        *win_lo = (win_l < 0 || win_l > fa::kUnbounded) ? fa::kUnbounded : win_l;
+        *win_hi = (win_r < 0 || win_r > fa::kUnbounded) ? fa::kUnbounded : win_r;
+        return true;
+    default:
+        return false;
+    }
+}
+
+bool overlaps(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) {
+    return a < b + nb && b < a + na;
+}
+
+}  // namespace
+
+extern "C" int64_t fa_visible_pairs(int S, int mask_mode, int win_l, int win_r) {
+    int win_lo, win_hi;
+    if (S < 0 || !window_of(mask_mode, win_l, win_r, &win_lo, &win_hi))
+        return FA_ERR_INVALID_ARG;
+    int64_t total = 0;
+    for (int64_t i = 0; i < S; ++i) {
+        int64_t lo, hi;
+        key_range(i, S, win_lo, win_hi, &lo, &hi);
+        if (hi >= lo) total += hi - lo + 1;
+    }
+    return total;
+}
+
+extern "C" int64_t fa_fwd_flops(int B, int H, int S, int D, int mask_mode, int win_l,
+                                int win_r) {
+    if (B < 0 || H < 0 || D <= 0) return FA_ERR_INVALID_ARG;
+    int64_t pairs = fa_visible_pairs(S, mask_mode, win_l, win_r);
+    if (pairs < 0) return pairs;
+    // 4 * D * B * H * pairs, refusing anything that does not fit in int64.
+    __int128 f = (__int128)4 * D * B * H * pairs;
+    if (f > (__int128)INT64_MAX) return FA_ERR_TOO_LARGE;
+    return (int64_t)f;
+}
+
+extern "C" const char *fa_strerror(int status) {
+    switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
+    case FA_ERR_ALIGNMENT: return "misaligned pointer (q/k/v/o need 16 bytes, lse 4)";
+    case FA_ERR_TOO_LARGE: return "problem too large for the kernel's index ranges";
+    case FA_ERR_HIP: return "HIP runtime error at kernel launch";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int B, int H, int S, int D, float scale, int mask_mode, int win_l,
+                      int win_r, int dtype, hipStream_t stream) {
+    // ---- scalar arguments -------------------------------------------------
+    if (B < 0 || H < 0 || S < 0) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    int win_lo, win_hi;
+    if (!window_of(mask_mode, win_l, win_r, &win_lo, &win_hi)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * S == 0) return FA_OK;  // nothing to compute, nothing read
+
+    // ---- sizes ------------------------------------------------------------
+    const uint64_t head_bytes = (uint64_t)S * D * 2;
+    if (head_bytes >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    const uint64_t bh = (uint64_t)B * H;
+    const uint64_t n_qtiles = ((uint64_t)S + fa::kBlockM - 1) / fa::kBlockM;
+    if (bh * n_qtiles > (uint64_t)INT32_MAX) return FA_ERR_TOO_LARGE;
+    const __int128 tensor_bytes = (__int128)bh * head_bytes;
+    if (tensor_bytes > (__int128)INT64_MAX / 4) return FA_ERR_TOO_LARGE;
+
+    // ---- pointers ---------------------------------------------------------
+    if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+    const uintptr_t pq = (uintptr_t)q, pk = (uintptr_t)k, pv = (uintptr_t)v,
+                    po = (uintptr_t)o, pl = (uintptr_t)lse;
+    if ((pq | pk | pv | po) & 15u) return FA_ERR_ALIGNMENT;
+    if (lse && (pl & 3u)) return FA_ERR_ALIGNMENT;
+    const uint64_t nbytes = (uint64_t)tensor_bytes;
+    const uint64_t lbytes = bh * (uint64_t)S * 4;
+    if (overlaps(po, nbytes, pq, nbytes) || overlaps(po, nbytes, pk, nbytes) ||
+        overlaps(po, nbytes, pv, nbytes))
+        return FA_ERR_INVALID_ARG;
+    if (lse && (overlaps(pl, lbytes, pq, nbytes) || overlaps(pl, lbytes, pk, nbytes) ||
+                overlaps(pl, lbytes, pv, nbytes) || overlaps(pl, lbytes, po, nbytes)))
+        return FA_ERR_INVALID_ARG;
+
+    // ---- launch -----------------------------------------------------------
+    fa::FwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.B = B;
+    p.H = H;
+    p.S = S;
+    p.n_qtiles = (int)n_qtiles;
+    p.win_lo = win_lo;
+    p.win_hi = win_hi;
+    p.c2 = std::fabs(scale) * 1.4426950408889634f;  // log2(e)
+    p.negate_q = scale < 0.0f;
+    p.xcd_remap = (bh % kNumXcd) == 0;
+    hipError_t err = fa::launch_fwd(p, D, dtype, stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

@@ -1,0 +1,35 @@
+// fa_internal.h -- launch parameters shared by the C-ABI host code and the
+// gfx950 kernels of the attention forward. Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace fa {
+
+// "Unbounded" window side: larger than any sequence index the ABI accepts,
+// small enough that i + kUnbounded does not overflow a 32-bit int.
+constexpr int kUnbounded = 1 << 30;
+
+// Everything a kernel needs, computed and validated on the host.
+struct FwdParams {
+    const void *q, *k, *v;  // [B, H, S, D]
+    void *o;                // [B, H, S, D]
+    float *lse;             // [B, H, S] or nullptr
+    int B, H, S;
+    int n_qtiles;           // ceil(S / query rows per workgroup)
+    // Key j is visible from query i iff i - win_lo <= j <= i + win_hi and j < S
+    // (win_lo, win_hi in [0, kUnbounded]); covers all three mask modes.
+    int win_lo, win_hi;
+    float c2;               // |scale| * log2(e): scores go to base 2 in one multiply
+    int negate_q;           // scale < 0: Q's sign is flipped on load instead
+    int xcd_remap;          // B*H is a multiple of the XCD count
+};
+
+// Query rows per workgroup of every kernel variant.
+constexpr int kBlockM = 128;
+
+// Enqueue the kernel for head dimension D and dtype (0 fp16, 1 bf16).
+hipError_t launch_fwd(const FwdParams &p, int D, int dtype, hipStream_t stream);
+
+}  // namespace fa
