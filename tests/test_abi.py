@@ -117,3 +117,10 @@ def test_forward_rejects_bad_tensors_on_cpu():
     with pytest.raises(ValueError):
         fa.forward(x.float(), x.float(), x.float())
     assert math.isclose(1 / math.sqrt(64), 0.125)
+
+
+def test_one_hip_runtime_in_process():
+    """libfa binds to the HIP runtime torch loaded, never to a second copy."""
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs

@@ -29,6 +29,13 @@ def lib_path():
 
 
 def _load():
+    # torch ships its own HIP runtime (SONAME libamdhip64.so.7). Loading torch
+    # first makes libfa bind to that same runtime instead of pulling a second
+    # copy from /opt/rocm, so torch's streams and pointers stay valid in libfa.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(

@@ -22,7 +22,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 def command(out=LIB, extra=()):
     return ([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-             "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"] + DEVICE_FLAGS + list(extra)
+             "-Wall", "-mcode-object-version=5", f"-I{INCLUDE}", f"-I{CSRC}"] + DEVICE_FLAGS + list(extra)
             + SOURCES + ["-o", out])
 
 
