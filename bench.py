@@ -103,8 +103,8 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the CPU oracle sample (0 = skip)")

@@ -1,0 +1,52 @@
+"""The comparison rule in tests/parity.py, on synthetic values (CPU only)."""
+import numpy as np
+
+from parity import compare, round_bf16, ulp_bf16
+from synth import f32_to_bits
+
+
+def _bits(x, dtype):
+    return f32_to_bits(np.asarray(x, np.float32), dtype)
+
+
+def test_exact_outputs_pass():
+    r = np.random.default_rng(0).standard_normal((64, 32))
+    for dtype in ("f16", "bf16"):
+        st = compare(_bits(r, dtype), None, r, None, dtype)
+        assert st["pass"], st
+
+
+def test_f16_bounds():
+    r = np.zeros((10, 10))
+    o = r.copy()
+    o[0, 0] = 2.5e-3
+    assert not compare(_bits(o, "f16"), None, r, None, "f16")["pass"]   # max
+    o = np.full((10, 10), 3e-4)
+    assert not compare(_bits(o, "f16"), None, r, None, "f16")["pass"]   # mean
+
+
+def test_bf16_one_ulp_allowed_two_not():
+    r = np.full((100, 100), 1.3)
+    R = round_bf16(r)
+    first = np.arange(r.size).reshape(r.shape) == 0
+    one = np.where(first, R + ulp_bf16(R), R)
+    two = np.where(first, R + 2 * ulp_bf16(R), R)
+    assert compare(_bits(one, "bf16"), None, r, None, "bf16")["pass"]
+    assert not compare(_bits(two, "bf16"), None, r, None, "bf16")["pass"]
+
+
+def test_bf16_small_values_use_absolute_bound():
+    r = np.full((100,), 0.01)
+    o = r.copy()
+    o[0] += 6e-3
+    assert not compare(_bits(o, "bf16"), None, r, None, "bf16")["pass"]
+
+
+def test_lse_and_nonfinite():
+    r = np.zeros((2, 2))
+    lse_ref = np.array([1.0, 2.0])
+    assert not compare(_bits(r, "f16"), np.array([1.0, 2.002]), r, lse_ref, "f16")["pass"]
+    assert compare(_bits(r, "f16"), np.array([1.0, 2.0005]), r, lse_ref, "f16")["pass"]
+    bad = r.copy()
+    bad[0, 0] = np.nan
+    assert not compare(_bits(bad, "f16"), None, r, None, "f16")["pass"]
