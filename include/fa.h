@@ -89,9 +89,9 @@ typedef enum {
  * needs no workspace and keeps no reference after return. o and lse must not
  * overlap q, k, v or each other (checked on the host).
  * Arithmetic: QK^T and PV run on fp16/bf16 matrix cores with fp32 accumulation;
- * softmax state is fp32; probabilities are rounded to `dtype` before PV and
- * the row sum uses the unrounded fp32 values. Results are bitwise
- * deterministic for a given input, device and library build.
+ * softmax state is fp32; probabilities are rounded once to `dtype` for PV
+ * while the row sum (and so the LSE) adds the unrounded fp32 values. Results
+ * are bitwise deterministic for a given input, device and library build.
  * Returns FA_OK or a negative fa_status.
  */
 int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -134,7 +134,12 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
     p.n_qtiles = (int)n_qtiles;
     p.win_lo = win_lo;
     p.win_hi = win_hi;
-    p.c2 = std::fabs(scale) * 1.4426950408889634f;  // log2(e)
+    // Scores go to base 2 in one multiply by c2 = |scale| * log2(e). c2 is
+    // floored at 2^-100: below that every visible score under 2^76 in
+    // magnitude (any fp16 input gives |q.k| < 2^40) maps to under 2^-24, so
+    // exp2 of it is exactly 1.0f, the same fp32 result as a zero scale, while
+    // c2 stays positive and hidden scores (-inf) keep probability exactly 0.
+    p.c2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);
     p.negate_q = scale < 0.0f;
     p.xcd_remap = (bh % kNumXcd) == 0;
     hipError_t err = fa::launch_fwd(p, D, dtype, stream);

@@ -21,7 +21,7 @@ struct FwdParams {
     // Key j is visible from query i iff i - win_lo <= j <= i + win_hi and j < S
     // (win_lo, win_hi in [0, kUnbounded]); covers all three mask modes.
     int win_lo, win_hi;
-    float c2;               // |scale| * log2(e): scores go to base 2 in one multiply
+    float c2;               // max(|scale| * log2(e), 2^-100): scores go to base 2 in one multiply
     int negate_q;           // scale < 0: Q's sign is flipped on load instead
     int xcd_remap;          // B*H is a multiple of the XCD count
 };

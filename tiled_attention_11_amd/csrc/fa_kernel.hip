@@ -4,9 +4,9 @@
 // What it computes: O = softmax(scale * Q K^T + mask) V and the row LSE, with
 // the online-softmax recurrence of the Ascend C FlashAttention-2 tile-fusion
 // page (ascendai.csdn.net), section 1.2: a running row maximum m and row sum l,
-// an unnormalised accumulator rescaled by exp(m_old - m_new) whenever m grows,
-// and one division by l at the end. Tiling Q into row blocks and streaming
-// K/V column blocks follows section 3 of that page and the ops-transformer
+// an unnormalised accumulator rescaled by exp(m_old - m_new) when m grows, and
+// one division by l at the end. Tiling Q into row blocks and streaming K/V
+// column blocks follows section 3 of that page and the ops-transformer
 // walkthrough (hwcomputing.csdn.net, 6a0ef689), "core idea: tiling + online
 // softmax"; skipping key blocks that the mask hides entirely follows section 6
 // of the tile-fusion page; the window mask follows the catlass article
@@ -17,20 +17,25 @@
 //    each wave owns 32 query rows for the whole key loop.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16
 //    (A = 32 keys x 16 dims, B = 16 dims x 32 queries). In the accumulator
-//    layout lane l then holds query (l % 32) and 16 keys, so the row max and
-//    row sum are in-lane reductions plus one exchange with lane l ^ 32, and
+//    layout lane l holds query l % 32 and 16 keys, so the row max and row sum
+//    are in-lane reductions plus one v_permlane32_swap with lane l ^ 32, and
 //    the per-row rescale of the output is a per-lane scalar.
-//  * The output is accumulated transposed as well, O^T += V^T P^T: P^T comes
+//  * The output is accumulated transposed too, O^T += V^T P^T: P^T comes
 //    straight out of the score accumulator (rounded to fp16/bf16) as the B
-//    operand, and V^T is the A operand, read from a transposed copy of the V
-//    tile in LDS.
-//  * K and V^T tiles are double-buffered in LDS: global loads of tile t+1 are
-//    issued before tile t is computed and written to the other buffer after,
-//    with one workgroup barrier per tile.
+//    operand; the V^T A operand is read from the row-major V tile with the
+//    transposing LDS load ds_read_b64_tr_b16 (a 16-lane group reads a 4 x 16
+//    block and each lane receives one column), so V is never transposed in
+//    registers.
+//  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds,
+//    16 bytes per lane, hardware zero-fill past the end of the sequence),
+//    double-buffered: tile t+1 streams in while tile t is computed, with one
+//    workgroup barrier per tile. No staging registers, no staging VALU.
+//  * LDS tiles are unpadded and XOR-swizzled per row in 16-byte chunks so that
+//    both the 16-byte K reads and the transposing V reads are free of bank
+//    conflicts on the 64-bank, 256 B/clk gfx950 LDS.
 //  * Key tiles that the mask hides from all 128 rows are never loaded; per
-//    wave, tiles hidden from its 32 rows are skipped, tiles fully visible run
-//    without any mask arithmetic, and only boundary tiles evaluate the
-//    per-element predicate.
+//    wave, tiles hidden from its 32 rows are skipped, fully visible tiles run
+//    without mask arithmetic, and only boundary tiles evaluate the predicate.
 //  * The flat workgroup index is remapped so that all query tiles of a head
 //    land on one XCD (workgroups are dealt round-robin over the 8 XCDs) and
 //    run heaviest-first (longest causal rows first).
@@ -50,63 +55,70 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+#define LDS __attribute__((address_space(3)))
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveRows = 32;  // query rows per wave
 static_assert(kWaves * kWaveRows == kBlockM, "workgroup covers kBlockM rows");
 
+// Word 3 of a gfx9 buffer resource for raw (untyped, stride 0) access.
+constexpr int kBufferFlags = 0x00020000;
+
 // ---- element type traits --------------------------------------------------
 template <typename T> struct Elem;
 template <> struct Elem<_Float16> {
     typedef f16x8 vec8;
+    typedef f16x2 vec2;
     static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
     // two fp32 -> two fp16, round to nearest even, packed low|high
     static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        f16x2 h = {(_Float16)a, (_Float16)b};
+        vec2 h = {(_Float16)a, (_Float16)b};
         return __builtin_bit_cast(uint32_t, h);
     }
 };
 template <> struct Elem<__bf16> {
     typedef bf16x8 vec8;
+    typedef bf16x2 vec2;
     static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        bf16x2 h = {(__bf16)a, (__bf16)b};
+        vec2 h = {(__bf16)a, (__bf16)b};
         return __builtin_bit_cast(uint32_t, h);
     }
 };
 
 // ---- tile geometry per head dimension ---------------------------------------
-// D = 128: 64-key tiles; D = 64: 128-key tiles. Both give 32 MFMAs per wave per
-// tile and 35 KiB of LDS per stage.
+// D = 128: 64-key tiles; D = 64: 128-key tiles. Either way a K or V tile is
+// 16 KiB, a wave issues 32 MFMAs per tile, and a stage (K + V) is 32 KiB.
 template <int D> struct Geom {
-    static constexpr int BN = (D == 128) ? 64 : 128;  // keys per tile
-    static constexpr int KS = D + 8;    // K tile row stride in elements (16 B pad)
-    static constexpr int VS = BN + 8;   // V^T tile row stride in elements (16 B pad)
-    static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = D * VS;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;   // elements per LDS stage
-    static constexpr int TPR = D / 8;                // threads per 16-byte-chunked row
-    static constexpr int KPT = BN * TPR / kThreads;  // keys each thread stages
-    static_assert(KPT == 4, "staging assumes 4 keys per thread");
-    static_assert((BN / 8) % 8 == 0, "V^T chunk swizzle needs 8-chunk groups");
-};
+    static constexpr int BN = (D == 128) ? 64 : 128;   // keys per tile
+    static constexpr int RB = 2 * D;                   // bytes per K/V row
+    static constexpr int CPR = RB / 16;                // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BN * RB;         // one K or V tile
+    static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K then V
+    static constexpr int ROWS_PER_KB = 1024 / RB;      // rows per 1 KiB DMA block
+    static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / kWaves;
+    static_assert(TILE_BYTES == 16384, "tile geometry");
+    static_assert(DMA_PER_WAVE * kWaves * 1024 == TILE_BYTES, "DMA split");
 
-// V^T rows hold the tile's keys in a permuted order: inside each group of 16
-// keys, key 8a + 4g + b (a, g in {0,1}, b in 0..3) sits at 8g + 4a + b. That
-// is the order in which lane group g = lane / 32 of a 32x32 score accumulator
-// holds its keys, so each lane's 8-key slice of P^T is one contiguous 16-byte
-// LDS read of V^T. In units of 4-key groups this swaps bits 0 and 1.
-__device__ __forceinline__ int vt_group_pos(int kg) {
-    return (kg & ~3) | ((kg & 1) << 1) | ((kg >> 1) & 1);
-}
-// 16-byte chunk swizzle of V^T rows: chunk c of row d lives at c ^ ((d >> 3) & 7),
-// so the 8-row-apart transposed writes hit different banks.
-__device__ __forceinline__ int vt_chunk(int chunk, int d) { return chunk ^ ((d >> 3) & 7); }
+    // Physical 16-byte chunk of logical chunk q in K row r: the 16 rows read
+    // together by one 16-lane group land on 16 different 4-bank groups.
+    static __device__ __forceinline__ int kchunk(int q, int r) {
+        return D == 128 ? (q ^ (r & 15)) : (q ^ ((r >> 1) & 7));
+    }
+    // Physical chunk of logical chunk q in V row r: the 4 rows x 64 bytes read
+    // by 32 lanes of a transposing load land in 4 different 64-byte segments.
+    static __device__ __forceinline__ int vchunk(int q, int r) {
+        return D == 128 ? (q ^ ((r & 3) << 2)) : (q ^ (((r >> 1) & 1) << 2));
+    }
+};
 
 template <typename T, int D>
 struct Kernel {
@@ -118,54 +130,111 @@ struct Kernel {
     static constexpr int NDB = D / 32;    // 32-dim output blocks
     static constexpr int NPC = BN / 16;   // 16-key chunks of the PV contraction
 
-    // Global -> registers: thread t stages keys 4*(t / TPR) + i, i = 0..3, at
-    // dims 8*(t % TPR) .. +7 of both K and V. Rows past S read as zero.
-    static __device__ __forceinline__ void load_tile(const uint16_t *kh, const uint16_t *vh,
-                                                     int k0, int S, u32x4 (&kr)[4],
-                                                     u32x4 (&vr)[4]) {
-        const int t = threadIdx.x;
-        const int kg = t / G::TPR, dc = t % G::TPR;
+    // Per-wave state carried across key tiles.
+    struct State {
+        vec8 qf[NDC];       // Q^T fragments (B operand): row r0 + l32, dims 16c + 8g .. +7
+        f32x16 oacc[NDB];   // O^T accumulator: lane holds query l32, dims of its C layout
+        float m_run;        // reference maximum of the base-2 scaled scores
+        float l_run;        // this lane's share of the row sum, relative to m_run
+    };
+
+    // Per-lane byte offsets, fixed for the whole key loop.
+    struct Addr {
+        uint32_t kdma[G::DMA_PER_WAVE];  // global offset of this lane's K chunk, per DMA block
+        uint32_t vdma[G::DMA_PER_WAVE];  // same for V (different swizzle)
+        uint32_t k[NDC];                 // LDS offset of the K fragment of chunk c, block 0
+        uint32_t v[NDB];                 // LDS offset of the V^T fragment of block db, chunk 0
+    };
+
+    // Largest growth of the row maximum absorbed without rescaling: while a
+    // row's new maximum stays within 2^8 of m_run, probabilities are taken
+    // relative to the stale m_run (values up to 256, exact in fp32 and normal
+    // in fp16/bf16), so O and l keep a common reference and the final O / l is
+    // unchanged. Only a larger jump (or the first tile) rescales.
+    static constexpr float kRescaleSlack = 8.0f;
+
+    static __device__ __forceinline__ float max_with_partner(float x) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, x);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]),
+                     __builtin_bit_cast(float, (uint32_t)r[1]));
+    }
+    static __device__ __forceinline__ float sum_with_partner(float x) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, x);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __builtin_bit_cast(float, (uint32_t)r[0]) +
+               __builtin_bit_cast(float, (uint32_t)r[1]);
+    }
+
+    static __device__ __forceinline__ void make_addr(Addr &ad, int wave, int lane) {
+        const int l32 = lane & 31, g = lane >> 5;
+        // DMA block b = DMA_PER_WAVE * wave + i fills tile rows
+        // [b * ROWS_PER_KB, +ROWS_PER_KB); lane L lands in physical chunk
+        // L % CPR of row L / CPR, so it fetches the logical chunk stored there.
+        const int pc = lane % G::CPR;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = k0 + 4 * kg + i;
-            if (key < S) {
-                const int64_t off = (int64_t)key * D + 8 * dc;
-                kr[i] = *reinterpret_cast<const u32x4 *>(kh + off);
-                vr[i] = *reinterpret_cast<const u32x4 *>(vh + off);
-            } else {
-                kr[i] = u32x4{0, 0, 0, 0};
-                vr[i] = u32x4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
+            const int row = (G::DMA_PER_WAVE * wave + i) * G::ROWS_PER_KB + lane / G::CPR;
+            ad.kdma[i] = row * G::RB + G::kchunk(pc, row) * 16;  // XOR swizzle is its own inverse
+            ad.vdma[i] = row * G::RB + G::vchunk(pc, row) * 16;
+        }
+        // K A operand, score block 0: row l32, logical chunk 2c + g.
+#pragma unroll
+        for (int c = 0; c < NDC; ++c)
+            ad.k[c] = l32 * G::RB + G::kchunk(2 * c + g, l32) * 16;
+        // V^T A operand (transposing read), key chunk 0, first half: lane in
+        // 16-lane group G16 = lane / 16 (g = G16 / 2, h = G16 % 2), q = lane % 16
+        // addresses row 4g + q / 4 and columns 32db + 16h + 4(q % 4) .. +3.
+        const int q = lane & 15, h = (lane >> 4) & 1;
+        const int vrow = 4 * g + (q >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + 16 * h + 4 * (q & 3);
+            ad.v[db] = vrow * G::RB + G::vchunk(col >> 3, vrow) * 16 + (col & 7) * 2;
         }
     }
 
-    // Registers -> LDS stage: K row-major (16-byte writes); V transposed, 4 keys
-    // of one dim per 8-byte write, keys permuted and chunks swizzled as above.
-    static __device__ __forceinline__ void store_tile(uint16_t *stage, const u32x4 (&kr)[4],
-                                                      const u32x4 (&vr)[4]) {
-        const int t = threadIdx.x;
-        const int kg = t / G::TPR, dc = t % G::TPR;
-        uint16_t *ks = stage;
-        uint16_t *vt = stage + G::K_ELEMS;
+    // Raw buffer resource (base, num_records bytes, stride 0) as 4 SGPRs.
+    static __device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+        const uint64_t a = (uint64_t)base;
+        return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes,
+                     kBufferFlags};
+    }
+
+    // 16 bytes per lane from the buffer at voffset straight into LDS at
+    // lds_base + 16 * lane (buffer_load_dwordx4 ... lds; offsets outside the
+    // resource read as zero). Issued from inline assembly so that the compiler
+    // does not guard every later LDS read with a wait for this load: the
+    // kernel orders DMA and LDS reads itself (vmcnt wait + barrier per tile).
+    // M0 carries the LDS base and is restored, with the one wait state the
+    // hardware needs between an SALU write of M0 and its use by the load.
+    static __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
+        uint32_t saved;
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(lds_base), "v"(voffset), "s"(rsrc)
+            : "memory");
+    }
+
+    // Stream one K tile and one V tile (rows k0 .. k0 + BN - 1) into an LDS
+    // stage. The buffer resources start at row k0 and end at row S, so rows
+    // past the sequence read as zero.
+    static __device__ __forceinline__ void load_tile(const uint16_t *kh, const uint16_t *vh,
+                                                     int k0, int S, uint32_t stage,
+                                                     const Addr &ad, int wave) {
+        const uint32_t bytes = (uint32_t)(S - k0) * G::RB;
+        const i32x4 kr = buffer_rsrc(kh + (int64_t)k0 * D, bytes);
+        const i32x4 vr = buffer_rsrc(vh + (int64_t)k0 * D, bytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4 *>(ks + (4 * kg + i) * G::KS + 8 * dc) = kr[i];
-        const int pos = 4 * vt_group_pos(kg);  // first of the 4 key slots
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = 8 * dc + e;
-            const int w = e >> 1;
-            uint32_t a0 = vr[0][w], a1 = vr[1][w], a2 = vr[2][w], a3 = vr[3][w];
-            u32x2 out;
-            if (e & 1) {
-                out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-            } else {
-                out[0] = (a0 & 0xffffu) | (a1 << 16);
-                out[1] = (a2 & 0xffffu) | (a3 << 16);
-            }
-            const int col = vt_chunk(pos >> 3, d) * 8 + (pos & 7);
-            *reinterpret_cast<u32x2 *>(vt + d * G::VS + col) = out;
+        for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
+            const uint32_t b = (uint32_t)(G::DMA_PER_WAVE * wave + i) * 1024u;
+            dma16(kr, stage + b, ad.kdma[i]);
+            dma16(vr, stage + G::TILE_BYTES + b, ad.vdma[i]);
         }
     }
 
@@ -184,12 +253,112 @@ struct Kernel {
         }
     }
 
-    static __device__ void run(const FwdParams &p, uint16_t *smem) {
+    // One key tile for one wave: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
+    // masked: evaluate the visibility predicate per element (boundary tiles);
+    // otherwise every (query, key) pair of the tile is visible.
+    static __device__ __forceinline__ void step(State &st, const LDS char *stage, const Addr &ad,
+                                                int k0, int qi, int S, int win_lo, int win_hi,
+                                                float c2, int g, bool masked) {
+        const LDS char *ks = stage;
+        const LDS char *vs = stage + G::TILE_BYTES;
+
+        // ---- S^T = K Q^T. Score blocks are 32 rows apart and 32 is a multiple
+        // of the K swizzle period, so block 0's offsets serve every block.
+        f32x16 sacc[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const vec8 a = *reinterpret_cast<const LDS vec8 *>(ks + ad.k[c] + kb * 32 * G::RB);
+                sacc[kb] = Elem<T>::mma(a, st.qf[c], sacc[kb]);
+            }
+        }
+
+        // ---- mask: accumulator element r of block kb holds key
+        // k0 + 32kb + 8(r/4) + 4g + r%4 for query qi. A hidden score becomes
+        // -inf; with c2 > 0 its probability exp2(-inf) is exactly 0.
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool ok = j < S && j <= qi + win_hi && j >= qi - win_lo;
+                    sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+                }
+        }
+
+        // ---- online softmax (base 2). c2 > 0, so the maximum of the scaled
+        // scores is c2 times the maximum score.
+        float smax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
+        smax = max_with_partner(smax);
+        const float m_tile = (smax == -INFINITY) ? -INFINITY : smax * c2;
+
+        if (__builtin_amdgcn_ballot_w64(m_tile > st.m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(st.m_run, m_tile);
+            const float alpha = (m_new == -INFINITY) ? 1.0f
+                                                     : __builtin_amdgcn_exp2f(st.m_run - m_new);
+            st.m_run = m_new;
+            st.l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) st.oacc[db] *= alpha;
+        }
+        const float mu = (st.m_run == -INFINITY) ? 0.0f : st.m_run;
+
+        // Probabilities: rounded once to the MFMA operand type for PV; the row
+        // sum adds the unrounded fp32 values (it also defines the LSE).
+        uint32_t pk[NKB][8];
+        float psum0 = 0.0f, psum1 = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -mu));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, -mu));
+                pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
+                psum0 += p0;
+                psum1 += p1;
+            }
+        st.l_run += psum0 + psum1;
+
+        // ---- O^T += V^T P^T over 16-key chunks c: B = P^T elements 8(c%2) ..
+        // +7 of score block c/2 (keys 16c + 8a + 4g + b for element 4a + b);
+        // A = V^T from two transposing reads, rows 16c + 4g + (0..3) and
+        // 16c + 8 + 4g + (0..3). Both row offsets are multiples of 4, which
+        // keeps the V swizzle of the lane's base row.
+#pragma unroll
+        for (int c = 0; c < NPC; ++c) {
+            const int kb = c >> 1, hh = c & 1;
+            const u32x4 pw = {pk[kb][4 * hh + 0], pk[kb][4 * hh + 1], pk[kb][4 * hh + 2],
+                              pk[kb][4 * hh + 3]};
+            const vec8 b = __builtin_bit_cast(vec8, pw);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const LDS char *base = vs + ad.v[db] + 16 * c * G::RB;
+                const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base));
+                const fp16x4_t hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base + 8 * G::RB));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                const vec8 a = __builtin_bit_cast(vec8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                st.oacc[db] = Elem<T>::mma(a, b, st.oacc[db]);
+            }
+        }
+    }
+
+    static __device__ void run(const FwdParams &p, LDS char *smem) {
         const int lane = threadIdx.x & 63;
-        const int wave = threadIdx.x >> 6;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int l32 = lane & 31;
         const int g = lane >> 5;
         const int S = p.S;
+        const int win_lo = p.win_lo, win_hi = p.win_hi;
 
         int bh, qt;
         tile_of(p, blockIdx.x, &bh, &qt);
@@ -200,149 +369,78 @@ struct Kernel {
 
         const int q0 = qt * kBlockM;
         const int qlast = min(q0 + kBlockM - 1, S - 1);
-        // Keys visible from any row of the workgroup, in whole tiles.
-        const int klo = max(0, q0 - p.win_lo);
-        const int khi = min(S - 1, qlast + p.win_hi);
-        const int t_first = klo / BN;
-        const int t_last = khi / BN;
+        // Keys visible from any row of the workgroup, in whole tiles; tiles
+        // outside are never loaded.
+        const int t_first = max(0, q0 - win_lo) / BN;
+        const int t_last = min(S - 1, qlast + win_hi) / BN;
+        // Tiles visible in full from every valid row of the workgroup:
+        // k0 >= qlast - win_lo and k0 + BN - 1 <= min(S - 1, q0 + win_hi).
+        const int t_in_lo = max(t_first, (max(0, qlast - win_lo) + BN - 1) / BN);
+        const int t_in_hi = (min(S - 1, q0 + win_hi) + 1) / BN;  // one past the last
 
         // This wave's rows and their visible key range.
         const int r0 = q0 + wave * kWaveRows;
         const bool wave_live = r0 < S;
         const int rlast = min(r0 + kWaveRows - 1, S - 1);
-        const int wklo = max(0, r0 - p.win_lo);
-        const int wkhi = min(S - 1, rlast + p.win_hi);
+        const int wklo = max(0, r0 - win_lo);
+        const int wkhi = min(S - 1, rlast + win_hi);
+        const int qi = r0 + l32;  // this lane's query row
 
-        // Q^T fragments (B operand): lane holds query row r0 + l32, dims
-        // 16c + 8g .. +7. Rows past S are zero.
-        vec8 qf[NDC];
+        Addr ad;
+        make_addr(ad, wave, lane);
+
+        // Start streaming the first tile before loading Q.
+        const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+        load_tile(kh, vh, t_first * BN, S, smem_addr, ad, wave);
+
+        State st;
         {
-            const int row = r0 + l32;
+            const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)qh, 0, (uint32_t)S * G::RB, kBufferFlags);
             const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
-                u32x4 x = u32x4{0, 0, 0, 0};
-                if (row < S)
-                    x = *reinterpret_cast<const u32x4 *>(qh + (int64_t)row * D + 16 * c + 8 * g);
+                // rows past S fall outside the resource and read as zero
+                u32x4 x = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               qr, (uint32_t)qi * G::RB + (16 * c + 8 * g) * 2, 0, 0));
                 x ^= flip;
-                qf[c] = __builtin_bit_cast(vec8, x);
+                st.qf[c] = __builtin_bit_cast(vec8, x);
             }
         }
-
-        f32x16 oacc[NDB];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-        float m_run = -INFINITY;  // running max of base-2 scaled scores
-        float l_run = 0.0f;       // this lane's share of the running row sum
+        for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
+        st.m_run = -INFINITY;
+        st.l_run = 0.0f;
         const float c2 = p.c2;
-        const int qi = r0 + l32;  // this lane's query row
 
-        u32x4 kr[4], vr[4];
-        load_tile(kh, vh, t_first * BN, S, kr, vr);
-        store_tile(smem, kr, vr);
+        __builtin_amdgcn_s_waitcnt(0);  // the first tile and Q have landed
         __syncthreads();
 
         for (int t = t_first; t <= t_last; ++t) {
-            uint16_t *stage = smem + ((t - t_first) & 1) * G::STAGE;
-            const bool more = t < t_last;
-            if (more) load_tile(kh, vh, (t + 1) * BN, S, kr, vr);
+            LDS char *stage = smem + ((t - t_first) & 1) * G::STAGE_BYTES;
+            if (t < t_last)
+                load_tile(kh, vh, (t + 1) * BN, S,
+                          smem_addr + ((t + 1 - t_first) & 1) * G::STAGE_BYTES, ad, wave);
 
             const int k0 = t * BN;
+            // Tiles inside [t_in_lo, t_in_hi) are fully visible to every row;
+            // elsewhere the wave classifies the tile against its own rows.
+            const bool interior = t >= t_in_lo && t < t_in_hi;
             const bool live = wave_live && k0 <= wkhi && k0 + BN - 1 >= wklo;
-            if (live) {
-                const bool full = k0 + BN - 1 <= S - 1 && k0 + BN - 1 <= r0 + p.win_hi &&
-                                  k0 >= rlast - p.win_lo;
-                const uint16_t *ks = stage;
-                const uint16_t *vt = stage + G::K_ELEMS;
+            const bool full = interior || (k0 + BN - 1 <= S - 1 && k0 + BN - 1 <= r0 + win_hi &&
+                                           k0 >= rlast - win_lo);
+            if (live) step(st, stage, ad, k0, qi, S, win_lo, win_hi, c2, g, !full);
 
-                // ---- S^T = K Q^T for this tile ----
-                f32x16 sacc[NKB];
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < NDC; ++c) {
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) {
-                        const vec8 a = *reinterpret_cast<const vec8 *>(
-                            ks + (32 * kb + l32) * G::KS + 16 * c + 8 * g);
-                        sacc[kb] = Elem<T>::mma(a, qf[c], sacc[kb]);
-                    }
-                }
-
-                // ---- mask (boundary tiles only) ----
-                // Accumulator element r of block kb holds key
-                // k0 + 32kb + 8(r/4) + 4g + r%4 for query qi.
-                uint64_t vis = ~0ull;
-                if (!full) {
-                    vis = 0;
-#pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                            const bool ok = j < S && j <= qi + p.win_hi && j >= qi - p.win_lo;
-                            vis |= (uint64_t)ok << (16 * kb + r);
-                            if (!ok) sacc[kb][r] = -INFINITY;
-                        }
-                }
-
-                // ---- online softmax (base 2) ----
-                float smax = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
-                smax = fmaxf(smax, __shfl_xor(smax, 32));
-                // c2 >= 0, so the max of the scaled scores is c2 * max(score).
-                const float m_tile = (smax == -INFINITY) ? -INFINITY : smax * c2;
-                const float m_new = fmaxf(m_run, m_tile);
-                const float mu = (m_new == -INFINITY) ? 0.0f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - mu);
-                m_run = m_new;
-
-                uint32_t pk[NKB][8];
-                float psum = 0.0f;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -mu));
-                        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, -mu));
-                        if (!full) {
-                            p0 = ((vis >> (16 * kb + r)) & 1) ? p0 : 0.0f;
-                            p1 = ((vis >> (16 * kb + r + 1)) & 1) ? p1 : 0.0f;
-                        }
-                        psum += p0 + p1;
-                        pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
-                    }
-                l_run = l_run * alpha + psum;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-
-                // ---- O^T += V^T P^T ----
-#pragma unroll
-                for (int c = 0; c < NPC; ++c) {
-                    const int kb = c >> 1, h = c & 1;
-                    const u32x4 pw = {pk[kb][4 * h + 0], pk[kb][4 * h + 1], pk[kb][4 * h + 2],
-                                      pk[kb][4 * h + 3]};
-                    const vec8 b = __builtin_bit_cast(vec8, pw);
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const int d = 32 * db + l32;
-                        const vec8 a = *reinterpret_cast<const vec8 *>(
-                            vt + d * G::VS + vt_chunk(2 * c + g, d) * 8);
-                        oacc[db] = Elem<T>::mma(a, b, oacc[db]);
-                    }
-                }
-            }
-
-            if (more) store_tile(smem + ((t + 1 - t_first) & 1) * G::STAGE, kr, vr);
+            // The next tile's DMA must have landed in LDS before anyone reads
+            // it, and this tile's stage must be drained before it is refilled.
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
 
         // ---- epilogue: O = O_acc / l, LSE = ln 2 * (m + log2 l) ----
         if (!wave_live || qi >= S) return;
-        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        const float l_tot = sum_with_partner(st.l_run);
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * D;
 #pragma unroll
@@ -351,12 +449,12 @@ struct Kernel {
             for (int a = 0; a < 4; ++a) {
                 // elements 4a .. 4a+3 hold dims 32db + 8a + 4g + 0..3
                 u32x2 w;
-                w[0] = Elem<T>::pack(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv);
-                w[1] = Elem<T>::pack(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv);
+                w[0] = Elem<T>::pack(st.oacc[db][4 * a + 0] * inv, st.oacc[db][4 * a + 1] * inv);
+                w[1] = Elem<T>::pack(st.oacc[db][4 * a + 2] * inv, st.oacc[db][4 * a + 3] * inv);
                 *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * a + 4 * g) = w;
             }
         if (p.lse && g == 0) {
-            const float lse = l_tot > 0.0f ? 0.69314718055994531f * (m_run + __log2f(l_tot))
+            const float lse = l_tot > 0.0f ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
                                            : -INFINITY;
             p.lse[(int64_t)bh * S + qi] = lse;
         }
@@ -365,8 +463,8 @@ struct Kernel {
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Geom<D>::STAGE];
-    Kernel<T, D>::run(p, smem);
+    __shared__ __attribute__((aligned(1024))) char smem[2 * Geom<D>::STAGE_BYTES];
+    Kernel<T, D>::run(p, (LDS char *)smem);
 }
 
 template <typename T, int D>
