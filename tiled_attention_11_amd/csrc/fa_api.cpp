@@ -141,7 +141,7 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
     // c2 stays positive and hidden scores (-inf) keep probability exactly 0.
     p.c2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);
     p.negate_q = scale < 0.0f;
-    p.xcd_remap = (bh % kNumXcd) == 0;
+    p.xcd_remap = (bh % (2 * kNumXcd)) == 0;  // pairs of heads per XCD
     hipError_t err = fa::launch_fwd(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -23,7 +23,7 @@ struct FwdParams {
     int win_lo, win_hi;
     float c2;               // max(|scale| * log2(e), 2^-100): scores go to base 2 in one multiply
     int negate_q;           // scale < 0: Q's sign is flipped on load instead
-    int xcd_remap;          // B*H is a multiple of the XCD count
+    int xcd_remap;          // B*H is a multiple of twice the XCD count
 };
 
 // Query rows per workgroup of every kernel variant.

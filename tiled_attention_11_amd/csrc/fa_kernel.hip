@@ -238,15 +238,21 @@ struct Kernel {
         }
     }
 
-    // Map the flat workgroup index to (b*H + h, query tile).
+    // Map the flat workgroup index to (b*H + h, query tile). Workgroups are
+    // dealt round-robin to the 8 XCDs (index % 8), so with B*H a multiple of 16
+    // XCD x runs heads x, x + 8, ... two at a time: the query tiles of each pair
+    // of heads are interleaved heaviest-first (longest causal rows first), which
+    // keeps two heads' K/V (2 x 2 MiB at S = 4096, D = 128) in the XCD's 4 MiB
+    // L2 and leaves only short tiles for the end of the launch.
     static __device__ __forceinline__ void tile_of(const FwdParams &p, int wg, int *bh,
                                                    int *qt) {
         const int nq = p.n_qtiles;
         if (p.xcd_remap) {
             const int xcd = wg & 7, slot = wg >> 3;
-            const int hl = slot / nq;
-            *bh = hl * 8 + xcd;
-            *qt = nq - 1 - (slot - hl * nq);
+            const int pair = slot / (2 * nq);
+            const int r = slot - pair * 2 * nq;
+            *bh = (2 * pair + (r & 1)) * 8 + xcd;
+            *qt = nq - 1 - (r >> 1);
         } else {
             *bh = wg / nq;
             *qt = nq - 1 - (wg - *bh * nq);
