@@ -27,7 +27,7 @@ struct FwdParams {
 };
 
 // Query rows per workgroup of every kernel variant.
-constexpr int kBlockM = 128;
+constexpr int kBlockM = 256;
 
 // Enqueue the kernel for head dimension D and dtype (0 fp16, 1 bf16).
 hipError_t launch_fwd(const FwdParams &p, int D, int dtype, hipStream_t stream);

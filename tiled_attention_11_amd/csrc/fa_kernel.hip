@@ -13,8 +13,14 @@
 // (lnwmold.com/news/1200460), section "usage".
 //
 // gfx950 design (not the pages' Ascend design):
-//  * One workgroup = 4 waves of 64 lanes = 128 query rows of one (b, h);
-//    each wave owns 32 query rows for the whole key loop.
+//  * One workgroup = 8 waves of 64 lanes = 256 query rows of one (b, h);
+//    each wave owns 32 query rows for the whole key loop. The waves form two
+//    groups (0-3 and 4-7, one wave of each per SIMD) that alternate, at
+//    workgroup barriers, between an MFMA phase (P V of the previous key tile,
+//    then the scores of the next) and a VALU phase (mask and online softmax),
+//    so that on every SIMD one wave keeps the matrix core busy while the other
+//    computes exponentials: a single wave cannot issue VALU work fast enough
+//    to hide it under its own MFMAs, but two waves of a SIMD co-issue.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16
 //    (A = 32 keys x 16 dims, B = 16 dims x 32 queries). In the accumulator
 //    layout lane l holds query l % 32 and 16 keys, so the row max and row sum
@@ -28,14 +34,15 @@
 //    registers.
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds,
 //    16 bytes per lane, hardware zero-fill past the end of the sequence),
-//    double-buffered: tile t+1 streams in while tile t is computed, with one
-//    workgroup barrier per tile. No staging registers, no staging VALU.
+//    double-buffered: each tile has two phases to land. No staging registers,
+//    no staging VALU.
 //  * LDS tiles are unpadded and XOR-swizzled per row in 16-byte chunks so that
 //    both the 16-byte K reads and the transposing V reads are free of bank
-//    conflicts on the 64-bank, 256 B/clk gfx950 LDS.
-//  * Key tiles that the mask hides from all 128 rows are never loaded; per
-//    wave, tiles hidden from its 32 rows are skipped, fully visible tiles run
-//    without mask arithmetic, and only boundary tiles evaluate the predicate.
+//    conflicts on the 64-bank gfx950 LDS.
+//  * Key tiles that the mask hides from all 256 rows are never loaded; every
+//    wave walks the same tiles (a tile hidden from a wave's rows is fully
+//    masked for it), fully visible tiles run without mask arithmetic, and only
+//    boundary tiles evaluate the predicate.
 //  * The flat workgroup index is remapped so that all query tiles of a head
 //    land on one XCD (workgroups are dealt round-robin over the 8 XCDs) and
 //    run heaviest-first (longest causal rows first).
@@ -60,9 +67,9 @@ typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
 #define LDS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;            // two groups of four, one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kWaveRows = 32;  // query rows per wave
+constexpr int kWaveRows = 32;        // query rows per wave
 static_assert(kWaves * kWaveRows == kBlockM, "workgroup covers kBlockM rows");
 
 // Word 3 of a gfx9 buffer resource for raw (untyped, stride 0) access.
@@ -102,7 +109,6 @@ template <int D> struct Geom {
     static constexpr int RB = 2 * D;                   // bytes per K/V row
     static constexpr int CPR = RB / 16;                // 16-byte chunks per row
     static constexpr int TILE_BYTES = BN * RB;         // one K or V tile
-    static constexpr int STAGE_BYTES = 2 * TILE_BYTES; // K then V
     static constexpr int ROWS_PER_KB = 1024 / RB;      // rows per 1 KiB DMA block
     static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / kWaves;
     static_assert(TILE_BYTES == 16384, "tile geometry");
@@ -136,6 +142,7 @@ struct Kernel {
         f32x16 oacc[NDB];   // O^T accumulator: lane holds query l32, dims of its C layout
         float m_run;        // reference maximum of the base-2 scaled scores
         float l_run;        // this lane's share of the row sum, relative to m_run
+        float alpha;        // pending rescale of oacc to the reference m_run
     };
 
     // Per-lane byte offsets, fixed for the whole key loop.
@@ -152,6 +159,25 @@ struct Kernel {
     // in fp16/bf16), so O and l keep a common reference and the final O / l is
     // unchanged. Only a larger jump (or the first tile) rescales.
     static constexpr float kRescaleSlack = 8.0f;
+
+    // MFMAs between an LDS operand read and its use in the MFMA phase.
+    static constexpr int kDist = 8;
+
+    // Materialise a value here: the compiler may not move its computation past
+    // this point (it would otherwise sink the softmax of one phase into the
+    // next, or the MFMAs of one phase past the barrier that ends it).
+    static __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+    static __device__ __forceinline__ void pin(f32x16 &x) { asm volatile("" : "+v"(x)); }
+    template <int N> static __device__ __forceinline__ void pin(f32x16 (&x)[N]) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) pin(x[n]);
+    }
+    template <int N, int M> static __device__ __forceinline__ void pin(uint32_t (&x)[N][M]) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+#pragma unroll
+            for (int m = 0; m < M; ++m) asm volatile("" : "+v"(x[n][m]));
+    }
 
     static __device__ __forceinline__ float max_with_partner(float x) {
         const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -221,21 +247,18 @@ struct Kernel {
             : "memory");
     }
 
-    // Stream one K tile and one V tile (rows k0 .. k0 + BN - 1) into an LDS
-    // stage. The buffer resources start at row k0 and end at row S, so rows
-    // past the sequence read as zero.
-    static __device__ __forceinline__ void load_tile(const uint16_t *kh, const uint16_t *vh,
-                                                     int k0, int S, uint32_t stage,
-                                                     const Addr &ad, int wave) {
-        const uint32_t bytes = (uint32_t)(S - k0) * G::RB;
-        const i32x4 kr = buffer_rsrc(kh + (int64_t)k0 * D, bytes);
-        const i32x4 vr = buffer_rsrc(vh + (int64_t)k0 * D, bytes);
+    // Stream one K or V tile (rows k0 .. k0 + BN - 1 of the head at `h`) into
+    // the LDS slot at byte address `slot`; `off` holds this lane's source
+    // offsets (which carry the matrix's swizzle). The buffer resource starts at
+    // row k0 and ends at row S, so rows past the sequence read as zero.
+    static __device__ __forceinline__ void load_tile(const uint16_t *h, int k0, int S,
+                                                     uint32_t slot,
+                                                     const uint32_t (&off)[G::DMA_PER_WAVE],
+                                                     int wave) {
+        const i32x4 rsrc = buffer_rsrc(h + (int64_t)k0 * D, (uint32_t)(S - k0) * G::RB);
 #pragma unroll
-        for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
-            const uint32_t b = (uint32_t)(G::DMA_PER_WAVE * wave + i) * 1024u;
-            dma16(kr, stage + b, ad.kdma[i]);
-            dma16(vr, stage + G::TILE_BYTES + b, ad.vdma[i]);
-        }
+        for (int i = 0; i < G::DMA_PER_WAVE; ++i)
+            dma16(rsrc, slot + (uint32_t)(G::DMA_PER_WAVE * wave + i) * 1024u, off[i]);
     }
 
     // Map the flat workgroup index to (b*H + h, query tile). Workgroups are
@@ -259,85 +282,24 @@ struct Kernel {
         }
     }
 
-    // One key tile for one wave: S^T = K Q^T, (mask), online softmax, O^T += V^T P^T.
-    // masked: evaluate the visibility predicate per element (boundary tiles);
-    // otherwise every (query, key) pair of the tile is visible.
-    static __device__ __forceinline__ void step(State &st, const LDS char *stage, const Addr &ad,
-                                                int k0, int qi, int S, int win_lo, int win_hi,
-                                                float c2, int g, bool masked) {
-        const LDS char *ks = stage;
-        const LDS char *vs = stage + G::TILE_BYTES;
+    // ---- phases -----------------------------------------------------------------
+    // The workgroup's eight waves form two groups (waves 0-3 and 4-7; one wave
+    // of each group per SIMD) that alternate between two kinds of work at
+    // workgroup barriers, so that on every SIMD one wave keeps the matrix core
+    // busy while the other runs the softmax on the VALU:
+    //   M_m: O^T += V^T P^T of tile m - 1, then S^T = K Q^T of tile m (MFMA);
+    //   V_m: mask, online softmax and P of tile m (VALU).
+    // A group runs M_0, V_0, M_1, V_1, ..., M_T; group 1 starts one phase after
+    // group 0. K(t) is read in phases 2t and 2t + 1, V(t) in 2t + 2 and 2t + 3;
+    // both stream in (DMA) two phases ahead and are double-buffered.
 
-        // ---- S^T = K Q^T. Score blocks are 32 rows apart and 32 is a multiple
-        // of the K swizzle period, so block 0's offsets serve every block.
-        f32x16 sacc[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < NDC; ++c) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const vec8 a = *reinterpret_cast<const LDS vec8 *>(ks + ad.k[c] + kb * 32 * G::RB);
-                sacc[kb] = Elem<T>::mma(a, st.qf[c], sacc[kb]);
-            }
-        }
-
-        // ---- mask: accumulator element r of block kb holds key
-        // k0 + 32kb + 8(r/4) + 4g + r%4 for query qi. A hidden score becomes
-        // -inf; with c2 > 0 its probability exp2(-inf) is exactly 0.
-        if (masked) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool ok = j < S && j <= qi + win_hi && j >= qi - win_lo;
-                    sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
-                }
-        }
-
-        // ---- online softmax (base 2). c2 > 0, so the maximum of the scaled
-        // scores is c2 times the maximum score.
-        float smax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
-        smax = max_with_partner(smax);
-        const float m_tile = (smax == -INFINITY) ? -INFINITY : smax * c2;
-
-        if (__builtin_amdgcn_ballot_w64(m_tile > st.m_run + kRescaleSlack)) {
-            const float m_new = fmaxf(st.m_run, m_tile);
-            const float alpha = (m_new == -INFINITY) ? 1.0f
-                                                     : __builtin_amdgcn_exp2f(st.m_run - m_new);
-            st.m_run = m_new;
-            st.l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) st.oacc[db] *= alpha;
-        }
-        const float mu = (st.m_run == -INFINITY) ? 0.0f : st.m_run;
-
-        // Probabilities: rounded once to the MFMA operand type for PV; the row
-        // sum adds the unrounded fp32 values (it also defines the LSE).
-        uint32_t pk[NKB][8];
-        float psum0 = 0.0f, psum1 = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -mu));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, -mu));
-                pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
-                psum0 += p0;
-                psum1 += p1;
-            }
-        st.l_run += psum0 + psum1;
-
-        // ---- O^T += V^T P^T over 16-key chunks c: B = P^T elements 8(c%2) ..
-        // +7 of score block c/2 (keys 16c + 8a + 4g + b for element 4a + b);
-        // A = V^T from two transposing reads, rows 16c + 4g + (0..3) and
-        // 16c + 8 + 4g + (0..3). Both row offsets are multiples of 4, which
-        // keeps the V swizzle of the lane's base row.
+    // O^T += V^T P^T for tile `vs`: chunk c's B operand is P^T elements
+    // 8(c%2) .. +7 of score block c/2 (keys 16c + 8a + 4g + b for element
+    // 4a + b); the A operand comes from two transposing reads, rows
+    // 16c + 4g + (0..3) and 16c + 8 + 4g + (0..3). Both row offsets are
+    // multiples of 4, which keeps the V swizzle of the lane's base row.
+    static __device__ __forceinline__ void pv(State &st, const uint32_t (&pk)[NKB][8],
+                                              const LDS char *vs, const Addr &ad) {
 #pragma unroll
         for (int c = 0; c < NPC; ++c) {
             const int kb = c >> 1, hh = c & 1;
@@ -358,9 +320,246 @@ struct Kernel {
         }
     }
 
+    // S^T = K Q^T for tile `ks`. Score blocks are 32 rows apart and 32 is a
+    // multiple of the K swizzle period, so block 0's offsets serve every block.
+    static __device__ __forceinline__ void qk(f32x16 (&sacc)[NKB], const State &st,
+                                              const LDS char *ks, const Addr &ad) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const vec8 a = *reinterpret_cast<const LDS vec8 *>(ks + ad.k[c] + kb * 32 * G::RB);
+                sacc[kb] = Elem<T>::mma(a, st.qf[c], sacc[kb]);
+            }
+        }
+    }
+
+    // Softmax of one tile: mask (boundary tiles), tile maximum, rescale of O
+    // and l when some row's maximum outgrows the slack (always on the first
+    // visible tile, where m_run is -inf), and the probabilities: rounded once
+    // to the MFMA operand type into pk, summed unrounded into l.
+    static __device__ __forceinline__ void softmax(State &st, f32x16 (&sacc)[NKB],
+                                                   uint32_t (&pk)[NKB][8], bool masked, int k0,
+                                                   int qi, int S, int win_lo, int win_hi,
+                                                   float c2, int g) {
+        // Accumulator element r of block kb holds key k0 + 32kb + 8(r/4) + 4g + r%4
+        // for query qi. A hidden score becomes -inf; with c2 > 0 its probability
+        // exp2(-inf) is exactly 0.
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool ok = j < S && j <= qi + win_hi && j >= qi - win_lo;
+                    sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
+                }
+        }
+        // c2 > 0, so the maximum of the scaled scores is c2 times the maximum score.
+        float smax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
+        smax = max_with_partner(smax);
+        const float m_tile = (smax == -INFINITY) ? -INFINITY : smax * c2;
+        // O is rescaled by the next MFMA phase (st.alpha), before its P V.
+        if (__builtin_amdgcn_ballot_w64(m_tile > st.m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(st.m_run, m_tile);
+            st.alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+            st.m_run = m_new;
+            st.l_run *= st.alpha;
+        }
+        const float mu = (st.m_run == -INFINITY) ? 0.0f : st.m_run;
+        float psum0 = 0.0f, psum1 = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -mu));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, -mu));
+                pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
+                psum0 += p0;
+                psum1 += p1;
+            }
+        st.l_run += psum0 + psum1;
+    }
+
+    // LDS: two K slots then two V slots; relative tile i uses slot i & 1.
+    static __device__ __forceinline__ uint32_t kslot(int i) { return (i & 1) * G::TILE_BYTES; }
+    static __device__ __forceinline__ uint32_t vslot(int i) {
+        return (2 + (i & 1)) * G::TILE_BYTES;
+    }
+
+    // The key loop of one wave. Global phases 0 .. 2T + 1 (T tiles) end at
+    // workgroup barriers. At phase 2i every wave issues its share of the DMA of
+    // K(i + 1) and V(i); at the end of phase 2i + 1 every wave waits for its own
+    // DMA, so after that barrier both tiles are in LDS. Group 0 runs M_i in
+    // phase 2i and V_i in phase 2i + 1; group 1 runs V_(i-1) in phase 2i and M_i
+    // in phase 2i + 1. K(i) is read in phases 2i and 2i + 1, V(i) in phases
+    // 2i + 2 and 2i + 3, so a slot is refilled only after both groups are done
+    // with its previous tile.
+    struct Loop {
+        const FwdParams &p;
+        const LDS char *smem;
+        uint32_t smem_addr;
+        const uint16_t *kh, *vh;
+        int S, t_first, ntiles, t_in_lo, t_in_hi, r0, rlast, qi, win_lo, win_hi;
+        float c2;
+        int g, wave;
+        const Addr &ad;
+
+        __device__ __forceinline__ bool tile_full(int t) const {
+            const int k0 = t * BN;
+            return (t >= t_in_lo && t < t_in_hi) ||
+                   (k0 + BN - 1 <= S - 1 && k0 + BN - 1 <= r0 + win_hi && k0 >= rlast - win_lo);
+        }
+        __device__ __forceinline__ void dma(int i) const {
+            if (i + 1 < ntiles)
+                load_tile(kh, (t_first + i + 1) * BN, S, smem_addr + kslot(i + 1), ad.kdma, wave);
+            if (i < ntiles)
+                load_tile(vh, (t_first + i) * BN, S, smem_addr + vslot(i), ad.vdma, wave);
+        }
+        // M_i: O takes the rescale the softmax of tile i - 1 asked for (a wave-
+        // uniform branch, rarely taken once the row maxima settle), then
+        // O^T += V^T P^T of tile i - 1 and S^T = K Q^T of tile i, as one stream
+        // of MFMAs whose LDS operands are read kDist MFMAs ahead.
+        template <bool QK, bool PV>
+        __device__ __forceinline__ void mphase(State &st, f32x16 (&sacc)[NKB],
+                                               const uint32_t (&pk)[NKB][8], int i) const {
+            __builtin_amdgcn_s_setprio(1);
+            if (PV && __builtin_amdgcn_ballot_w64(st.alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) st.oacc[db] *= st.alpha;
+                st.alpha = 1.0f;
+            }
+            const LDS char *vs = smem + vslot(i - 1);
+            const LDS char *ks = smem + kslot(i);
+            constexpr int NPV = PV ? NPC * NDB : 0;  // MFMA slot s < NPV: P V chunk s / NDB, block s % NDB
+            constexpr int NQK = QK ? NDC * NKB : 0;  // then S^T chunk q / NKB, block q % NKB
+            constexpr int NS = NPV + NQK;
+            vec8 a[NS];
+            auto load = [&](int s) {
+                if (s < NPV) {
+                    const int c = s / NDB, db = s % NDB;
+                    const LDS char *base = vs + ad.v[db] + 16 * c * G::RB;
+                    const fp16x4_t lo =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base));
+                    const fp16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                        (LDS fp16x4_t *)(base + 8 * G::RB));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+                    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+                    a[s] = __builtin_bit_cast(vec8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+                } else {
+                    const int q = s - NPV, c = q / NKB, kb = q % NKB;
+                    a[s] = *reinterpret_cast<const LDS vec8 *>(ks + ad.k[c] + kb * 32 * G::RB);
+                }
+            };
+            auto mma = [&](int s) {
+                if (s < NPV) {
+                    const int c = s / NDB, db = s % NDB, kb = c >> 1, hh = c & 1;
+                    const u32x4 pw = {pk[kb][4 * hh + 0], pk[kb][4 * hh + 1], pk[kb][4 * hh + 2],
+                                      pk[kb][4 * hh + 3]};
+                    st.oacc[db] = Elem<T>::mma(a[s], __builtin_bit_cast(vec8, pw), st.oacc[db]);
+                } else {
+                    const int q = s - NPV, c = q / NKB, kb = q % NKB;
+                    sacc[kb] = Elem<T>::mma(a[s], st.qf[c], c == 0 ? f32x16{} : sacc[kb]);
+                }
+            };
+#pragma unroll
+            for (int s = 0; s < kDist && s < NS; ++s) load(s);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (s + kDist < NS) load(s + kDist);
+                mma(s);
+            }
+            // Issue order: the first kDist reads, then per slot its look-ahead
+            // read(s) and its MFMA.
+#pragma unroll
+            for (int s = 0; s < kDist && s < NS; ++s) {
+                if (s < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (s + kDist < NS) {
+                    if (s + kDist < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+            }
+            if (QK) pin(sacc);
+            if (PV) pin(st.oacc);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        __device__ __forceinline__ void vphase(State &st, f32x16 (&sacc)[NKB],
+                                               uint32_t (&pk)[NKB][8], int i) const {
+            const int t = t_first + i;
+            softmax(st, sacc, pk, !tile_full(t), t * BN, qi, S, win_lo, win_hi, c2, g);
+            pin(pk);
+            pin(st.l_run);
+            pin(st.m_run);
+            pin(st.alpha);
+        }
+        // A bare barrier: the kernel orders its own LDS traffic. Every LDS read
+        // of a phase has returned before the phase ends (the pinned MFMA
+        // results consumed them), so a slot may be refilled after the barrier;
+        // DMA'd tiles are waited for (vmcnt) only at the end of odd phases,
+        // which leaves each DMA two phases to land.
+        static __device__ __forceinline__ void end_phase(bool wait) {
+            if (wait) __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_barrier();
+        }
+
+        template <int GRP>
+        __device__ __forceinline__ void go(State &st) const {
+            f32x16 sacc[NKB];
+            uint32_t pk[NKB][8];
+            const int nt = ntiles;  // >= 1
+            if (GRP == 0) {
+                dma(0);
+                mphase<true, false>(st, sacc, pk, 0);
+                end_phase(false);
+                vphase(st, sacc, pk, 0);
+                end_phase(true);
+                for (int i = 1; i < nt; ++i) {
+                    dma(i);
+                    mphase<true, true>(st, sacc, pk, i);
+                    end_phase(false);
+                    vphase(st, sacc, pk, i);
+                    end_phase(true);
+                }
+                dma(nt);
+                mphase<false, true>(st, sacc, pk, nt);
+                end_phase(false);
+                end_phase(true);
+            } else {
+                dma(0);
+                end_phase(false);
+                mphase<true, false>(st, sacc, pk, 0);
+                end_phase(true);
+                for (int i = 1; i < nt; ++i) {
+                    dma(i);
+                    vphase(st, sacc, pk, i - 1);
+                    end_phase(false);
+                    mphase<true, true>(st, sacc, pk, i);
+                    end_phase(true);
+                }
+                dma(nt);
+                vphase(st, sacc, pk, nt - 1);
+                end_phase(false);
+                mphase<false, true>(st, sacc, pk, nt);
+                end_phase(true);
+            }
+        }
+    };
+
     static __device__ void run(const FwdParams &p, LDS char *smem) {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7
         const int l32 = lane & 31;
         const int g = lane >> 5;
         const int S = p.S;
@@ -376,28 +575,26 @@ struct Kernel {
         const int q0 = qt * kBlockM;
         const int qlast = min(q0 + kBlockM - 1, S - 1);
         // Keys visible from any row of the workgroup, in whole tiles; tiles
-        // outside are never loaded.
+        // outside are never loaded. Every wave walks all of them: a tile hidden
+        // from a wave's rows is simply fully masked for that wave.
         const int t_first = max(0, q0 - win_lo) / BN;
         const int t_last = min(S - 1, qlast + win_hi) / BN;
+        const int ntiles = t_last - t_first + 1;
         // Tiles visible in full from every valid row of the workgroup:
         // k0 >= qlast - win_lo and k0 + BN - 1 <= min(S - 1, q0 + win_hi).
         const int t_in_lo = max(t_first, (max(0, qlast - win_lo) + BN - 1) / BN);
         const int t_in_hi = (min(S - 1, q0 + win_hi) + 1) / BN;  // one past the last
 
-        // This wave's rows and their visible key range.
+        // This wave's rows.
         const int r0 = q0 + wave * kWaveRows;
-        const bool wave_live = r0 < S;
         const int rlast = min(r0 + kWaveRows - 1, S - 1);
-        const int wklo = max(0, r0 - win_lo);
-        const int wkhi = min(S - 1, rlast + win_hi);
         const int qi = r0 + l32;  // this lane's query row
 
         Addr ad;
         make_addr(ad, wave, lane);
 
-        // Start streaming the first tile before loading Q.
         const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
-        load_tile(kh, vh, t_first * BN, S, smem_addr, ad, wave);
+        load_tile(kh, t_first * BN, S, smem_addr + kslot(0), ad.kdma, wave);
 
         State st;
         {
@@ -418,34 +615,20 @@ struct Kernel {
         for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
         st.m_run = -INFINITY;
         st.l_run = 0.0f;
+        st.alpha = 1.0f;
         const float c2 = p.c2;
-
-        __builtin_amdgcn_s_waitcnt(0);  // the first tile and Q have landed
+        __builtin_amdgcn_s_waitcnt(0);  // K of the first tile and Q have landed
         __syncthreads();
 
-        for (int t = t_first; t <= t_last; ++t) {
-            LDS char *stage = smem + ((t - t_first) & 1) * G::STAGE_BYTES;
-            if (t < t_last)
-                load_tile(kh, vh, (t + 1) * BN, S,
-                          smem_addr + ((t + 1 - t_first) & 1) * G::STAGE_BYTES, ad, wave);
-
-            const int k0 = t * BN;
-            // Tiles inside [t_in_lo, t_in_hi) are fully visible to every row;
-            // elsewhere the wave classifies the tile against its own rows.
-            const bool interior = t >= t_in_lo && t < t_in_hi;
-            const bool live = wave_live && k0 <= wkhi && k0 + BN - 1 >= wklo;
-            const bool full = interior || (k0 + BN - 1 <= S - 1 && k0 + BN - 1 <= r0 + win_hi &&
-                                           k0 >= rlast - win_lo);
-            if (live) step(st, stage, ad, k0, qi, S, win_lo, win_hi, c2, g, !full);
-
-            // The next tile's DMA must have landed in LDS before anyone reads
-            // it, and this tile's stage must be drained before it is refilled.
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
+        Loop loop{p, smem, smem_addr, kh, vh, S, t_first, ntiles, t_in_lo, t_in_hi, r0,
+                  rlast, qi, win_lo, win_hi, c2, g, wave, ad};
+        if (grp == 0)
+            loop.template go<0>(st);
+        else
+            loop.template go<1>(st);
 
         // ---- epilogue: O = O_acc / l, LSE = ln 2 * (m + log2 l) ----
-        if (!wave_live || qi >= S) return;
+        if (qi >= S) return;
         const float l_tot = sum_with_partner(st.l_run);
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * D;
@@ -468,8 +651,8 @@ struct Kernel {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(FwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * Geom<D>::STAGE_BYTES];
+__global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[4 * Geom<D>::TILE_BYTES];
     Kernel<T, D>::run(p, (LDS char *)smem);
 }
 
