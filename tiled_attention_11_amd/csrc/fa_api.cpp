@@ -141,7 +141,28 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
     // c2 stays positive and hidden scores (-inf) keep probability exactly 0.
     p.c2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);
     p.negate_q = scale < 0.0f;
-    p.xcd_remap = (bh % (2 * kNumXcd)) == 0;  // pairs of heads per XCD
+
+    // One workgroup per CU (each takes a whole CU), each running its share of
+    // the bh * n_qtiles query tiles; see FwdParams.
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu <= 0)
+        return FA_ERR_HIP;
+    const uint64_t n_items = bh * n_qtiles;
+    uint64_t grid = n_items < (uint64_t)n_cu ? n_items : (uint64_t)n_cu;
+    const bool xcd = bh % kNumXcd == 0 && grid >= (uint64_t)kNumXcd;
+    if (xcd) grid -= grid % kNumXcd;
+    const uint64_t list_heads = xcd ? bh / kNumXcd : bh;
+    const uint64_t nj = xcd ? grid / kNumXcd : grid;  // workgroups per list
+    // Heads per group: enough that a round of nj positions covers about one
+    // group, so the workgroups of a list share few heads at a time.
+    uint64_t gh = 1;
+    while (2 * gh * n_qtiles <= nj && list_heads % (2 * gh) == 0) gh *= 2;
+    p.grid = (int)grid;
+    p.xcd_lists = xcd;
+    p.list_len = (int)(list_heads * n_qtiles);
+    p.group_heads = (int)gh;
     hipError_t err = fa::launch_fwd(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -23,7 +23,15 @@ struct FwdParams {
     int win_lo, win_hi;
     float c2;               // max(|scale| * log2(e), 2^-100): scores go to base 2 in one multiply
     int negate_q;           // scale < 0: Q's sign is flipped on load instead
-    int xcd_remap;          // B*H is a multiple of twice the XCD count
+    // Work distribution (see the kernel): `grid` workgroups, each running a
+    // stream of work items (query tiles). xcd_lists: B*H % 8 == 0 and grid % 8
+    // == 0, so list x (heads x, x + 8, ...) is served by workgroups w = x mod 8;
+    // otherwise one list holds every head. list_len: items per list;
+    // group_heads: heads per group within a list (divides the list's heads).
+    int grid;
+    int xcd_lists;
+    int list_len;
+    int group_heads;
 };
 
 // Query rows per workgroup of every kernel variant.

@@ -80,6 +80,15 @@ template <typename T> struct Elem;
 template <> struct Elem<_Float16> {
     typedef f16x8 vec8;
     typedef f16x2 vec2;
+    // The row sum adds the fp16-rounded probabilities (the P V operands), two
+    // per v_dot2 against (1, 1), in the MFMA phase; their rounding (relative
+    // 2^-12 at most) moves the LSE by under 2.5e-4.
+    static constexpr bool kSumRounded = true;
+    // acc + a.lo + a.hi for two packed fp16 values
+    static __device__ __forceinline__ float sum2(uint32_t a, float acc) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), one, acc, false);
+    }
     static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
@@ -92,6 +101,10 @@ template <> struct Elem<_Float16> {
 template <> struct Elem<__bf16> {
     typedef bf16x8 vec8;
     typedef bf16x2 vec2;
+    // bf16 rounding (relative 2^-9) would move the LSE by up to 2e-3: the row
+    // sum adds the unrounded fp32 probabilities in the softmax instead.
+    static constexpr bool kSumRounded = false;
+    static __device__ __forceinline__ float sum2(uint32_t, float acc) { return acc; }
     static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
@@ -261,25 +274,67 @@ struct Kernel {
             dma16(rsrc, slot + (uint32_t)(G::DMA_PER_WAVE * wave + i) * 1024u, off[i]);
     }
 
-    // Map the flat workgroup index to (b*H + h, query tile). Workgroups are
-    // dealt round-robin to the 8 XCDs (index % 8), so with B*H a multiple of 16
-    // XCD x runs heads x, x + 8, ... two at a time: the query tiles of each pair
-    // of heads are interleaved heaviest-first (longest causal rows first), which
-    // keeps two heads' K/V (2 x 2 MiB at S = 4096, D = 128) in the XCD's 4 MiB
-    // L2 and leaves only short tiles for the end of the launch.
-    static __device__ __forceinline__ void tile_of(const FwdParams &p, int wg, int *bh,
-                                                   int *qt) {
+    // ---- work items -------------------------------------------------------------
+    // A work item is one query tile (kBlockM rows) of one (b, h). The grid has
+    // at most one workgroup per CU and workgroup w runs its items r = 0, 1, ...
+    // back to back as one stream of key tiles. Items are laid out in lists:
+    // with B*H a multiple of 8, list x holds the heads x, x + 8, x + 16, ... and
+    // is served only by the workgroups w = x (mod 8), which the dispatcher
+    // places on XCD x, so a head's K and V are read into one XCD's L2 and reused
+    // there by all its query tiles. Within a list, heads go in groups of
+    // group_heads, heaviest query tile (longest causal rows) first; round r hands
+    // positions r*nj .. r*nj + nj - 1 to the nj workgroups of the list, in
+    // reverse order on odd rounds, so that a workgroup given a heavy tile in one
+    // round gets a light one in the next.
+    struct Item {
+        int bh, q0;     // head (b*H + h) and first query row
+        int t_first;    // first key tile the workgroup's rows can see
+        int nt;         // number of key tiles; 0 marks "no such item"
+        int t_in_lo, t_in_hi;  // [t_in_lo, t_in_hi): tiles visible in full from every row
+    };
+
+    static __device__ __forceinline__ Item item_of(const FwdParams &p, int r) {
+        Item it;
         const int nq = p.n_qtiles;
-        if (p.xcd_remap) {
-            const int xcd = wg & 7, slot = wg >> 3;
-            const int pair = slot / (2 * nq);
-            const int r = slot - pair * 2 * nq;
-            *bh = (2 * pair + (r & 1)) * 8 + xcd;
-            *qt = nq - 1 - (r >> 1);
-        } else {
-            *bh = wg / nq;
-            *qt = nq - 1 - (wg - *bh * nq);
+        const int w = blockIdx.x;
+        int x = 0, j = w, nj = (int)gridDim.x;
+        if (p.xcd_lists) {
+            x = w & 7;
+            j = w >> 3;
+            nj = (int)gridDim.x >> 3;
         }
+        const int pos = r * nj + ((r & 1) ? nj - 1 - j : j);
+        if (pos >= p.list_len) {
+            it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = 0;
+            return it;
+        }
+        const int gh = p.group_heads;
+        const int per_group = gh * nq;
+        const int grp = pos / per_group, within = pos - grp * per_group;
+        const int qt = nq - 1 - within / gh;
+        const int hl = grp * gh + within % gh;
+        it.bh = p.xcd_lists ? hl * 8 + x : hl;
+        const int S = p.S;
+        it.q0 = qt * kBlockM;
+        const int qlast = min(it.q0 + kBlockM - 1, S - 1);
+        // Keys visible from any row of the item, in whole tiles; tiles outside
+        // are never loaded. Every wave walks all of them: a tile hidden from a
+        // wave's rows is simply fully masked for that wave.
+        it.t_first = max(0, it.q0 - p.win_lo) / BN;
+        const int t_last = min(S - 1, qlast + p.win_hi) / BN;
+        it.nt = t_last - it.t_first + 1;
+        // Tiles visible in full from every valid row of the item:
+        // k0 >= qlast - win_lo and k0 + BN - 1 <= min(S - 1, q0 + win_hi).
+        it.t_in_lo = max(it.t_first, (max(0, qlast - p.win_lo) + BN - 1) / BN);
+        it.t_in_hi = (min(S - 1, it.q0 + p.win_hi) + 1) / BN;  // one past the last
+        // Uniform across the workgroup: keep it in scalar registers.
+        it.bh = __builtin_amdgcn_readfirstlane(it.bh);
+        it.q0 = __builtin_amdgcn_readfirstlane(it.q0);
+        it.t_first = __builtin_amdgcn_readfirstlane(it.t_first);
+        it.nt = __builtin_amdgcn_readfirstlane(it.nt);
+        it.t_in_lo = __builtin_amdgcn_readfirstlane(it.t_in_lo);
+        it.t_in_hi = __builtin_amdgcn_readfirstlane(it.t_in_hi);
+        return it;
     }
 
     // ---- phases -----------------------------------------------------------------
@@ -381,10 +436,12 @@ struct Kernel {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -mu));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, -mu));
                 pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
-                psum0 += p0;
-                psum1 += p1;
+                if (!Elem<T>::kSumRounded) {
+                    psum0 += p0;
+                    psum1 += p1;
+                }
             }
-        st.l_run += psum0 + psum1;
+        if (!Elem<T>::kSumRounded) st.l_run += psum0 + psum1;
     }
 
     // LDS: two K slots then two V slots; relative tile i uses slot i & 1.
@@ -490,6 +547,20 @@ struct Kernel {
                 }
                 __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
             }
+            // The row sum of tile i - 1 from its rounded probabilities (fp16): VALU
+            // work that issues between this wave's MFMAs.
+            if (PV && Elem<T>::kSumRounded) {
+                float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 8; r += 2) {
+                        s0 = Elem<T>::sum2(pk[kb][r], s0);
+                        s1 = Elem<T>::sum2(pk[kb][r + 1], s1);
+                    }
+                st.l_run += s0 + s1;
+                pin(st.l_run);
+            }
             if (QK) pin(sacc);
             if (PV) pin(st.oacc);
             __builtin_amdgcn_s_setprio(0);
@@ -564,88 +635,83 @@ struct Kernel {
         const int g = lane >> 5;
         const int S = p.S;
         const int win_lo = p.win_lo, win_hi = p.win_hi;
-
-        int bh, qt;
-        tile_of(p, blockIdx.x, &bh, &qt);
-        const int64_t head = (int64_t)bh * S * D;
-        const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
-        const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
-        const uint16_t *vh = static_cast<const uint16_t *>(p.v) + head;
-
-        const int q0 = qt * kBlockM;
-        const int qlast = min(q0 + kBlockM - 1, S - 1);
-        // Keys visible from any row of the workgroup, in whole tiles; tiles
-        // outside are never loaded. Every wave walks all of them: a tile hidden
-        // from a wave's rows is simply fully masked for that wave.
-        const int t_first = max(0, q0 - win_lo) / BN;
-        const int t_last = min(S - 1, qlast + win_hi) / BN;
-        const int ntiles = t_last - t_first + 1;
-        // Tiles visible in full from every valid row of the workgroup:
-        // k0 >= qlast - win_lo and k0 + BN - 1 <= min(S - 1, q0 + win_hi).
-        const int t_in_lo = max(t_first, (max(0, qlast - win_lo) + BN - 1) / BN);
-        const int t_in_hi = (min(S - 1, q0 + win_hi) + 1) / BN;  // one past the last
-
-        // This wave's rows.
-        const int r0 = q0 + wave * kWaveRows;
-        const int rlast = min(r0 + kWaveRows - 1, S - 1);
-        const int qi = r0 + l32;  // this lane's query row
-
+        const float c2 = p.c2;
+        const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
         Addr ad;
         make_addr(ad, wave, lane);
 
-        const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
-        load_tile(kh, t_first * BN, S, smem_addr + kslot(0), ad.kdma, wave);
+        // The workgroup's items, one after the other. Every item ends with a
+        // workgroup barrier after its last LDS read, so the next one may
+        // refill any slot.
+        for (int r = 0;; ++r) {
+            const Item it = item_of(p, r);
+            if (it.nt == 0) break;
+            const int64_t head = (int64_t)it.bh * S * D;
+            const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
+            const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
+            const uint16_t *vh = static_cast<const uint16_t *>(p.v) + head;
 
-        State st;
-        {
-            const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)qh, 0, (uint32_t)S * G::RB, kBufferFlags);
-            const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
+            // This wave's rows.
+            const int r0 = it.q0 + wave * kWaveRows;
+            const int rlast = min(r0 + kWaveRows - 1, S - 1);
+            const int qi = r0 + l32;  // this lane's query row
+
+            load_tile(kh, it.t_first * BN, S, smem_addr + kslot(0), ad.kdma, wave);
+
+            State st;
+            {
+                const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)qh, 0, (uint32_t)S * G::RB, kBufferFlags);
+                const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
 #pragma unroll
-            for (int c = 0; c < NDC; ++c) {
-                // rows past S fall outside the resource and read as zero
-                u32x4 x = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               qr, (uint32_t)qi * G::RB + (16 * c + 8 * g) * 2, 0, 0));
-                x ^= flip;
-                st.qf[c] = __builtin_bit_cast(vec8, x);
+                for (int c = 0; c < NDC; ++c) {
+                    // rows past S fall outside the resource and read as zero
+                    u32x4 x = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   qr, (uint32_t)qi * G::RB + (16 * c + 8 * g) * 2, 0, 0));
+                    x ^= flip;
+                    st.qf[c] = __builtin_bit_cast(vec8, x);
+                }
             }
-        }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
-        st.m_run = -INFINITY;
-        st.l_run = 0.0f;
-        st.alpha = 1.0f;
-        const float c2 = p.c2;
-        __builtin_amdgcn_s_waitcnt(0);  // K of the first tile and Q have landed
-        __syncthreads();
+            for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
+            st.m_run = -INFINITY;
+            st.l_run = 0.0f;
+            st.alpha = 1.0f;
+            __builtin_amdgcn_s_waitcnt(0);  // K of the first tile and Q have landed
+            __syncthreads();
 
-        Loop loop{p, smem, smem_addr, kh, vh, S, t_first, ntiles, t_in_lo, t_in_hi, r0,
-                  rlast, qi, win_lo, win_hi, c2, g, wave, ad};
-        if (grp == 0)
-            loop.template go<0>(st);
-        else
-            loop.template go<1>(st);
+            Loop loop{p, smem, smem_addr, kh, vh, S, it.t_first, it.nt, it.t_in_lo, it.t_in_hi,
+                      r0, rlast, qi, win_lo, win_hi, c2, g, wave, ad};
+            if (grp == 0)
+                loop.template go<0>(st);
+            else
+                loop.template go<1>(st);
 
-        // ---- epilogue: O = O_acc / l, LSE = ln 2 * (m + log2 l) ----
-        if (qi >= S) return;
-        const float l_tot = sum_with_partner(st.l_run);
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * D;
+            // ---- epilogue: O = O_acc / l, LSE = ln 2 * (m + log2 l) ----
+            const float l_tot = sum_with_partner(st.l_run);
+            if (qi < S) {
+                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+                uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                // elements 4a .. 4a+3 hold dims 32db + 8a + 4g + 0..3
-                u32x2 w;
-                w[0] = Elem<T>::pack(st.oacc[db][4 * a + 0] * inv, st.oacc[db][4 * a + 1] * inv);
-                w[1] = Elem<T>::pack(st.oacc[db][4 * a + 2] * inv, st.oacc[db][4 * a + 3] * inv);
-                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * a + 4 * g) = w;
+                    for (int a = 0; a < 4; ++a) {
+                        // elements 4a .. 4a+3 hold dims 32db + 8a + 4g + 0..3
+                        u32x2 w;
+                        w[0] = Elem<T>::pack(st.oacc[db][4 * a + 0] * inv,
+                                             st.oacc[db][4 * a + 1] * inv);
+                        w[1] = Elem<T>::pack(st.oacc[db][4 * a + 2] * inv,
+                                             st.oacc[db][4 * a + 3] * inv);
+                        *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * a + 4 * g) = w;
+                    }
+                if (p.lse && g == 0) {
+                    const float lse = l_tot > 0.0f
+                                          ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
+                                          : -INFINITY;
+                    p.lse[(int64_t)it.bh * S + qi] = lse;
+                }
             }
-        if (p.lse && g == 0) {
-            const float lse = l_tot > 0.0f ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
-                                           : -INFINITY;
-            p.lse[(int64_t)bh * S + qi] = lse;
         }
     }
 };
@@ -658,9 +724,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdParams p) {
 
 template <typename T, int D>
 hipError_t launch_t(const FwdParams &p, hipStream_t stream) {
-    const int grid = p.B * p.H * p.n_qtiles;
     void *args[] = {const_cast<FwdParams *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_fwd_kernel<T, D>), dim3(grid),
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_fwd_kernel<T, D>), dim3(p.grid),
                            dim3(kThreads), args, 0, stream);
 }
 
