@@ -89,8 +89,9 @@ typedef enum {
  * needs no workspace and keeps no reference after return. o and lse must not
  * overlap q, k, v or each other (checked on the host).
  * Arithmetic: QK^T and PV run on fp16/bf16 matrix cores with fp32 accumulation;
- * softmax state is fp32; probabilities are rounded once to `dtype` for PV
- * while the row sum (and so the LSE) adds the unrounded fp32 values. Results
+ * softmax state is fp32; probabilities are rounded once to `dtype` for PV. The
+ * row sum (and so the LSE) adds, in fp32, the fp16-rounded probabilities for
+ * fp16 (an LSE change below 2.5e-4) and the unrounded ones for bf16. Results
  * are bitwise deterministic for a given input, device and library build.
  * Returns FA_OK or a negative fa_status.
  */
