@@ -446,6 +446,32 @@ struct Kernel {
 
     // LDS: two K slots then two V slots; relative tile i uses slot i & 1.
     static __device__ __forceinline__ uint32_t kslot(int i) { return (i & 1) * G::TILE_BYTES; }
+    // After the four tile slots: Q of the workgroup's next item, kBlockM rows in
+    // the K swizzle; wave w's rows 32w .. 32w + 31 are written (DMA) and read
+    // by wave w only.
+    static constexpr uint32_t kQRegion = 4 * G::TILE_BYTES;
+    static constexpr int kQBlocks = kWaveRows * G::RB / 1024;  // 1 KiB DMA blocks per wave
+
+    // DMA this wave's 32 rows of the item's Q (rows past S read as zero) into
+    // its part of the Q region. Lane L of 1 KiB block b lands in physical
+    // chunk L % CPR of region row b * ROWS_PER_KB + L / CPR, so it fetches the
+    // logical chunk that the K swizzle stores there.
+    static __device__ __forceinline__ void dma_q(const uint16_t *qh, int q0, int S,
+                                                 uint32_t smem_addr, int wave, int lane) {
+        const int r0 = q0 + wave * kWaveRows;
+        // A wave whose rows all lie past S gets an empty resource: every read
+        // returns zero and nothing past the tensor is touched.
+        const uint32_t rows = r0 < S ? (uint32_t)(S - r0) : 0u;
+        const i32x4 rsrc = buffer_rsrc(qh + (int64_t)r0 * D, rows * G::RB);
+        const uint32_t base = smem_addr + kQRegion + (uint32_t)(wave * kWaveRows) * G::RB;
+        const int pc = lane % G::CPR;
+#pragma unroll
+        for (int b = 0; b < kQBlocks; ++b) {
+            const int row = b * G::ROWS_PER_KB + lane / G::CPR;
+            dma16(rsrc, base + (uint32_t)b * 1024u,
+                  (uint32_t)(row * G::RB + G::kchunk(pc, row) * 16));
+        }
+    }
     static __device__ __forceinline__ uint32_t vslot(int i) {
         return (2 + (i & 1)) * G::TILE_BYTES;
     }
@@ -465,19 +491,32 @@ struct Kernel {
         const uint16_t *kh, *vh;
         int S, t_first, ntiles, t_in_lo, t_in_hi, r0, rlast, qi, win_lo, win_hi;
         float c2;
-        int g, wave;
+        int g, wave, lane;
         const Addr &ad;
+        int kbase;             // slot parity of this item's tile 0
+        const Item &nx;        // the workgroup's next item (nx.nt == 0: none)
 
         __device__ __forceinline__ bool tile_full(int t) const {
             const int k0 = t * BN;
             return (t >= t_in_lo && t < t_in_hi) ||
                    (k0 + BN - 1 <= S - 1 && k0 + BN - 1 <= r0 + win_hi && k0 >= rlast - win_lo);
         }
+        // Phase 2i: K(i + 1) (after the last tile, the next item's K(0), in the
+        // slot its parity continues into) and V(i); at phase 2 also the next
+        // item's Q (this item's Q has been read from the Q region by then).
         __device__ __forceinline__ void dma(int i) const {
             if (i + 1 < ntiles)
-                load_tile(kh, (t_first + i + 1) * BN, S, smem_addr + kslot(i + 1), ad.kdma, wave);
+                load_tile(kh, (t_first + i + 1) * BN, S, smem_addr + kslot(kbase + i + 1),
+                          ad.kdma, wave);
+            else if (i + 1 == ntiles && nx.nt > 0)
+                load_tile(static_cast<const uint16_t *>(p.k) + (int64_t)nx.bh * S * D,
+                          nx.t_first * BN, S, smem_addr + kslot(kbase + ntiles), ad.kdma, wave);
             if (i < ntiles)
-                load_tile(vh, (t_first + i) * BN, S, smem_addr + vslot(i), ad.vdma, wave);
+                load_tile(vh, (t_first + i) * BN, S, smem_addr + vslot(kbase + i), ad.vdma,
+                          wave);
+            if (i == 1 && nx.nt > 0)
+                dma_q(static_cast<const uint16_t *>(p.q) + (int64_t)nx.bh * S * D, nx.q0, S,
+                      smem_addr, wave, lane);
         }
         // M_i: O takes the rescale the softmax of tile i - 1 asked for (a wave-
         // uniform branch, rarely taken once the row maxima settle), then
@@ -492,8 +531,8 @@ struct Kernel {
                 for (int db = 0; db < NDB; ++db) st.oacc[db] *= st.alpha;
                 st.alpha = 1.0f;
             }
-            const LDS char *vs = smem + vslot(i - 1);
-            const LDS char *ks = smem + kslot(i);
+            const LDS char *vs = smem + vslot(kbase + i - 1);
+            const LDS char *ks = smem + kslot(kbase + i);
             constexpr int NPV = PV ? NPC * NDB : 0;  // MFMA slot s < NPV: P V chunk s / NDB, block s % NDB
             constexpr int NQK = QK ? NDC * NKB : 0;  // then S^T chunk q / NKB, block q % NKB
             constexpr int NS = NPV + NQK;
@@ -641,13 +680,22 @@ struct Kernel {
         make_addr(ad, wave, lane);
 
         // The workgroup's items, one after the other. Every item ends with a
-        // workgroup barrier after its last LDS read, so the next one may
-        // refill any slot.
-        for (int r = 0;; ++r) {
-            const Item it = item_of(p, r);
-            if (it.nt == 0) break;
+        // workgroup barrier after its last LDS read and its wait for its DMA,
+        // which includes the next item's K(0) and Q: the next item starts
+        // with them in LDS.
+        Item it = item_of(p, 0);  // every workgroup has at least one item
+        {
+            const uint16_t *h = static_cast<const uint16_t *>(p.k) + (int64_t)it.bh * S * D;
+            load_tile(h, it.t_first * BN, S, smem_addr + kslot(0), ad.kdma, wave);
+            dma_q(static_cast<const uint16_t *>(p.q) + (int64_t)it.bh * S * D, it.q0, S, smem_addr,
+                  wave, lane);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        int kbase = 0;
+        for (int r = 0; it.nt > 0; ++r) {
+            const Item nx = item_of(p, r + 1);
             const int64_t head = (int64_t)it.bh * S * D;
-            const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
             const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
             const uint16_t *vh = static_cast<const uint16_t *>(p.v) + head;
 
@@ -656,19 +704,15 @@ struct Kernel {
             const int rlast = min(r0 + kWaveRows - 1, S - 1);
             const int qi = r0 + l32;  // this lane's query row
 
-            load_tile(kh, it.t_first * BN, S, smem_addr + kslot(0), ad.kdma, wave);
-
+            // Q^T fragments from the Q region: the B-operand fragment of chunk c
+            // is row l32, logical chunk 2c + g, the K read pattern.
             State st;
             {
-                const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)qh, 0, (uint32_t)S * G::RB, kBufferFlags);
+                const LDS char *qs = smem + kQRegion + wave * kWaveRows * G::RB;
                 const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
 #pragma unroll
                 for (int c = 0; c < NDC; ++c) {
-                    // rows past S fall outside the resource and read as zero
-                    u32x4 x = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                   qr, (uint32_t)qi * G::RB + (16 * c + 8 * g) * 2, 0, 0));
+                    u32x4 x = *reinterpret_cast<const LDS u32x4 *>(qs + ad.k[c]);
                     x ^= flip;
                     st.qf[c] = __builtin_bit_cast(vec8, x);
                 }
@@ -678,11 +722,9 @@ struct Kernel {
             st.m_run = -INFINITY;
             st.l_run = 0.0f;
             st.alpha = 1.0f;
-            __builtin_amdgcn_s_waitcnt(0);  // K of the first tile and Q have landed
-            __syncthreads();
 
-            Loop loop{p, smem, smem_addr, kh, vh, S, it.t_first, it.nt, it.t_in_lo, it.t_in_hi,
-                      r0, rlast, qi, win_lo, win_hi, c2, g, wave, ad};
+            Loop loop{p,  smem,  smem_addr, kh,    vh, S, it.t_first, it.nt, it.t_in_lo, it.t_in_hi,
+                      r0, rlast, qi,        win_lo, win_hi, c2, g, wave, lane, ad, kbase, nx};
             if (grp == 0)
                 loop.template go<0>(st);
             else
@@ -712,13 +754,15 @@ struct Kernel {
                     p.lse[(int64_t)it.bh * S + qi] = lse;
                 }
             }
+            kbase += it.nt;
+            it = nx;
         }
     }
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[4 * Geom<D>::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[4 * Geom<D>::TILE_BYTES + kBlockM * Geom<D>::RB];
     Kernel<T, D>::run(p, (LDS char *)smem);
 }
 
