@@ -39,6 +39,10 @@ def _bind(lib):
         _ptr, _ptr, _ptr, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64, _i64,
         ctypes.c_int, _ptr, _ptr, _ptr]
     lib.oracle_attention_probs.restype = ctypes.c_int
+    lib.oracle_attention_kv.argtypes = [
+        _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int,
+        _i64, _i64, ctypes.c_int, _ptr, _ptr, ctypes.c_int]
+    lib.oracle_attention_kv.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [_ptr, _i64, ctypes.c_int, _ptr]
     lib.oracle_decode.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -128,6 +132,32 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_attention_probs rejected its arguments")
         return p, o, lse
+
+    def attention_kv(self, q, k, v, dtype, scale, mask, window=(-1, -1), nthreads=0):
+        """New query rows against a key/value cache (incremental decoding).
+
+        ``q``: [B, H, Sq, D]; ``k, v``: [B, H, Sk, D] (uint16 bit patterns),
+        1 <= Sq <= Sk. Query row i sits at position Sk - Sq + i. Returns
+        ``(o [B,H,Sq,D] float64, lse [B,H,Sq] float64)``.
+        """
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+        if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+            raise ValueError("q must be [B, H, Sq, D] and k, v one [B, H, Sk, D] shape")
+        B, H, Sq, D = q.shape
+        if k.shape[:2] != (B, H) or k.shape[3] != D:
+            raise ValueError("q and k, v disagree on B, H or D")
+        Sk = k.shape[2]
+        m, wl, wr = self._mask_args(mask, window)
+        o = np.empty((B, H, Sq, D), dtype=np.float64)
+        lse = np.empty((B, H, Sq), dtype=np.float64)
+        rc = self.lib.oracle_attention_kv(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Sq, Sk, D, float(scale), m,
+            wl, wr, _DTYPES[dtype], o.ctypes.data, lse.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_attention_kv rejected its arguments")
+        return o, lse
 
     def max_threads(self):
         return int(self.lib.oracle_max_threads())

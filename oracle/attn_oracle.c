@@ -143,16 +143,18 @@ static int check_args(int64_t B, int64_t H, int64_t S, int64_t D, int mask_mode,
     return 0;
 }
 
-/* One query row of one head: materialise the score row, then two passes.
- * qh, kh, vh point at the head's [S, D] block. srow (S doubles), qrow and
- * orow (D doubles each) are scratch owned by the caller. */
-static void one_row(const uint16_t *qh, const uint16_t *kh, const uint16_t *vh,
+/* One query row against S keys: materialise the score row, then two passes.
+ * qsrc points at the query row's D values, kh and vh at the head's [S, D] key
+ * and value blocks; i is the query's position in the sequence, which the mask
+ * compares with the key positions 0 .. S-1. srow (S doubles), qrow and orow (D
+ * doubles each) are scratch owned by the caller. */
+static void one_row(const uint16_t *qsrc, const uint16_t *kh, const uint16_t *vh,
                     int64_t S, int64_t D, double scale, int mask_mode, int64_t wl,
                     int64_t wr, int dtype, int64_t i, double *srow, double *qrow,
                     double *orow, double *o_out, double *lse_out)
 {
     for (int64_t d = 0; d < D; ++d)
-        qrow[d] = decode(qh[i * D + d], dtype);
+        qrow[d] = decode(qsrc[d], dtype);
 
     /* Scores (Ascend C tile-fusion page, section 1.1; the NPU optimisation
      * page, section "core idea: IO-aware": QK^T times the scale). Masked
@@ -243,7 +245,7 @@ int oracle_attention_rows(const uint16_t *q, const uint16_t *k, const uint16_t *
                 int64_t bh = rows[r] / S;
                 int64_t i = rows[r] % S;
                 const int64_t base = bh * S * D;
-                one_row(q + base, k + base, v + base, S, D, scale, mask_mode, wl, wr,
+                one_row(q + base + i * D, k + base, v + base, S, D, scale, mask_mode, wl, wr,
                         dtype, i, srow, qrow, orow, o + r * D, lse + r);
             }
         }
@@ -271,7 +273,7 @@ int oracle_attention_probs(const uint16_t *qh, const uint16_t *kh, const uint16_
     }
     for (int64_t i = 0; i < S; ++i) {
         double *srow = p + i * S;
-        one_row(qh, kh, vh, S, D, scale, mask_mode, wl, wr, dtype, i, srow, qrow, orow,
+        one_row(qh + i * D, kh, vh, S, D, scale, mask_mode, wl, wr, dtype, i, srow, qrow, orow,
                 o + i * D, lse + i);
         /* one_row leaves the scores in srow; turn them into probabilities. */
         double m = -INFINITY;
@@ -290,6 +292,62 @@ int oracle_attention_probs(const uint16_t *qh, const uint16_t *kh, const uint16_
     free(qrow);
     free(orow);
     return 0;
+}
+
+/* New query rows against a key/value cache (incremental decoding).
+ * q is [B,H,Sq,D]; k and v are [B,H,Sk,D] and hold the first Sk positions of
+ * each sequence, the new rows' own keys included; o is [B,H,Sq,D] and lse is
+ * [B,H,Sq], both fp64. Query row i sits at position Sk - Sq + i (the new rows
+ * are the last Sq positions), and key j is visible from it under the rules of
+ * oracle_visible at that position. Everything else is the definition above.
+ * Reading: the NPU optimisation page (hwcomputing.csdn.net, 6a0fe629),
+ * section "optimisation 4: KV-cache reuse", computes the attention of the new
+ * token against the cached keys and values of its sequence, and its hands-on
+ * section (step 3) feeds a [1, 32, 1, 128] query against a [1, 32, 50, 128]
+ * cache. The code printed there attends to the last cached key only and then
+ * averages outputs, which is not attention; the plain reading is attention of
+ * each new row over every visible cached key, which is what this computes.
+ * Requires 1 <= Sq <= Sk. nthreads <= 0 uses the OpenMP default.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_attention_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                        double scale, int mask_mode, int64_t wl, int64_t wr, int dtype,
+                        double *o, double *lse, int nthreads)
+{
+    if (check_args(B, H, Sk, D, mask_mode, dtype)) return -1;
+    if (Sq < 1 || Sq > Sk) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    const int64_t n_rows = B * H * Sq;
+    int failed = 0;
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+    {
+        double *srow = (double *)malloc(sizeof(double) * (size_t)Sk);
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)D);
+        double *orow = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!srow || !qrow || !orow) {
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                const int64_t bh = r / Sq, i = r % Sq;
+#if ORACLE_PLANT == 7
+                const int64_t pos = i;                 /* planted: top-left alignment */
+#else
+                const int64_t pos = Sk - Sq + i;
+#endif
+                one_row(q + r * D, k + bh * Sk * D, v + bh * Sk * D, Sk, D, scale,
+                        mask_mode, wl, wr, dtype, pos, srow, qrow, orow, o + r * D, lse + r);
+            }
+        }
+        free(srow);
+        free(qrow);
+        free(orow);
+    }
+    return failed ? -1 : 0;
 }
 
 /* Decode n raw 16-bit values to fp64 with the oracle's own decoders. */

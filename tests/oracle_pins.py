@@ -318,6 +318,87 @@ def pin_scale_is_a_multiplier(orc):
     assert np.max(np.abs(a[0] - b[0])) < 1e-12 and np.max(np.abs(a[1] - b[1])) < 1e-12
 
 
+# --------------------------------------------------------------------------
+# new rows against a key/value cache (incremental decoding)
+
+KV_SHAPES = [(1, 1), (1, 37), (3, 3), (5, 64), (16, 100), (16, 16), (32, 70)]
+
+
+def _bool_mask_kv(Sq, Sk, mask, window):
+    """Visibility of Sk cached keys from Sq new rows placed at the end of the
+    sequence (row i at position Sk - Sq + i), with numpy index arithmetic."""
+    i = (Sk - Sq) + np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    if mask == "full":
+        return np.ones((Sq, Sk), dtype=bool)
+    if mask == "causal":
+        return j <= i
+    wl, wr = window
+    ok = np.ones((Sq, Sk), dtype=bool)
+    if wl >= 0:
+        ok &= j >= i - wl
+    if wr >= 0:
+        ok &= j <= i + wr
+    return ok
+
+
+def pin_kv_sdpa(orc):
+    """Cache attention matches torch's CPU fp64 scaled_dot_product_attention
+    with a rectangular bottom-right boolean mask, and torch.logsumexp."""
+    rng = np.random.default_rng(31)
+    for dtype in ("f16", "bf16"):
+        for (Sq, Sk) in KV_SHAPES:
+            D = 16
+            q, _, _ = make_qkv(2, 2, Sq, D, dtype, seed=int(rng.integers(1 << 30)))
+            _, k, v = make_qkv(2, 2, Sk, D, dtype, seed=int(rng.integers(1 << 30)))
+            qd = torch.from_numpy(_decode_ref(q, dtype))
+            kd = torch.from_numpy(_decode_ref(k, dtype))
+            vd = torch.from_numpy(_decode_ref(v, dtype))
+            for mask, window in MASK_CASES:
+                bm = _bool_mask_kv(Sq, Sk, mask, window)
+                if not bm.any(axis=1).all():
+                    continue  # a row with no visible key: covered by the definition only
+                scale = 0.35
+                bmt = torch.from_numpy(bm)
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qd, kd, vd, attn_mask=bmt, scale=scale).numpy()
+                scores = torch.matmul(qd, kd.transpose(-1, -2)) * scale
+                lse_ref = torch.logsumexp(scores.masked_fill(~bmt, float("-inf")), dim=-1).numpy()
+                o, lse = orc.attention_kv(q, k, v, dtype, scale, mask, window)
+                assert np.max(np.abs(o - ref)) < 1e-12, (dtype, Sq, Sk, mask, window)
+                assert np.max(np.abs(lse - lse_ref)) < 1e-12, (dtype, Sq, Sk, mask, window)
+
+
+def pin_kv_is_the_tail_of_the_square_case(orc):
+    """New rows at the end of a sequence give the last rows of the square
+    problem whose query rows end with them (any earlier query rows)."""
+    rng = np.random.default_rng(32)
+    for (Sq, Sk) in ((1, 50), (7, 40), (16, 16)):
+        Q, k, v = make_qkv(1, 3, Sk, 8, "f16", seed=int(rng.integers(1 << 30)))
+        q = np.ascontiguousarray(Q[:, :, Sk - Sq:, :])
+        for mask, window in (("causal", (-1, -1)), ("window", (4, 0)), ("full", (-1, -1))):
+            o_sq, lse_sq = orc.attention(Q, k, v, "f16", 0.5, mask, window)
+            o, lse = orc.attention_kv(q, k, v, "f16", 0.5, mask, window)
+            assert np.max(np.abs(o - o_sq[:, :, Sk - Sq:, :])) < 1e-13, (Sq, Sk, mask)
+            assert np.max(np.abs(lse - lse_sq[:, :, Sk - Sq:])) < 1e-13, (Sq, Sk, mask)
+
+
+def pin_kv_uniform_weights(orc):
+    """Q = 0: each new row's output is the plain mean of the V rows it can see,
+    and its LSE is the log of how many there are (closed form, numpy)."""
+    Sq, Sk, D = 6, 29, 8
+    q = _bits(np.zeros((1, 1, Sq, D)))
+    _, k, v = make_qkv(1, 1, Sk, D, "f16", seed=33)
+    vd = _decode_ref(v, "f16")[0, 0]
+    for mask, window in MASK_CASES:
+        vis = _bool_mask_kv(Sq, Sk, mask, window)
+        o, lse = orc.attention_kv(q, k, v, "f16", 0.7, mask, window)
+        for i in range(Sq):
+            n = int(vis[i].sum())
+            assert abs(lse[0, 0, i] - math.log(n)) < 1e-12, (mask, window, i)
+            assert np.max(np.abs(o[0, 0, i] - vd[vis[i]].mean(axis=0))) < 1e-12, (mask, i)
+
+
 ALL_PINS = [
     pin_decoders,
     pin_pair_counts,
@@ -334,4 +415,7 @@ ALL_PINS = [
     pin_mask_equivalences,
     pin_probabilities,
     pin_scale_is_a_multiplier,
+    pin_kv_sdpa,
+    pin_kv_is_the_tail_of_the_square_case,
+    pin_kv_uniform_weights,
 ]
