@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the fused attention forward on AMD Instinct MI355X (gfx950).
+ * fa.h -- C ABI of the fused attention forward (and of the attention of new query
+ * rows against a key/value cache) on AMD Instinct MI355X (gfx950).
  *
  * Computes, for every batch b, head h and query row i,
  *     O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,h,j,:] + mask_ij) V[b,h,j,:]
@@ -22,7 +23,8 @@
  *     ops-transformer walkthrough, pitfall 3, and the tile-fusion page,
  *     section 10 (best practice).
  *
- * All functions are reentrant and thread-safe; the library keeps no state.
+ * All functions are reentrant and thread-safe; the library keeps no state and
+ * allocates no memory (fa_decode's workspace is the caller's).
  */
 #ifndef FA_H
 #define FA_H
@@ -112,6 +114,62 @@ int64_t fa_visible_pairs(int S, int mask_mode, int win_l, int win_r);
  * negative fa_status.
  */
 int64_t fa_fwd_flops(int B, int H, int S, int D, int mask_mode, int win_l, int win_r);
+
+/*
+ * fa_decode -- attention of Sq new query rows against a key/value cache
+ * (incremental decoding): O = softmax(scale * Q K^T + mask) V, where query row i
+ * sits at position Sk - Sq + i of its sequence and the cache holds positions
+ * 0 .. Sk-1, the new rows' own keys included; the mask rules of fa_fwd apply at
+ * that position (so FA_MASK_CAUSAL lets row i see keys 0 .. Sk - Sq + i).
+ * Defining passage: "FlashAttention on Ascend NPU: from principle to practice"
+ * (hwcomputing.csdn.net, 6a0fe629), section "optimisation 4: KV-cache reuse",
+ * read as attention of each new row over every visible cached key.
+ *
+ * q        device pointer, contiguous [B, H, Sq, D] of `dtype`; read only.
+ * k, v     device pointers, contiguous [B, H, Sk, D] of `dtype` (the cache); read only.
+ * o        device pointer, [B, H, Sq, D] of `dtype`; fully overwritten (RNE).
+ * lse      device pointer to fp32 [B, H, Sq] (natural log), or NULL.
+ * B, H     >= 0. Sq: 0 .. 32 query rows, Sq <= Sk. If B*H*Sq == 0 the call does
+ *          nothing and returns FA_OK. D: 64 or 128. scale, mask_mode, win_l,
+ *          win_r, dtype, stream: as for fa_fwd.
+ * workspace, workspace_bytes
+ *          device memory for per-split partial results, at least
+ *          fa_decode_workspace_bytes(...) bytes and 16-byte aligned; may be NULL
+ *          when that size is 0. Owned by the caller; the call only uses it
+ *          until the enqueued work completes; its contents on entry do not
+ *          matter and on exit are unspecified.
+ *
+ * The visible cache range of each head is cut into splits processed by
+ * separate workgroups; each writes its normalised partial output and LSE to
+ * the workspace and a second kernel merges the splits of each row,
+ * LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s. The number of
+ * splits depends on the shape and the current device's CU count, so call
+ * fa_decode_workspace_bytes with the same device current. Same arithmetic,
+ * determinism, ownership and error rules as fa_fwd; additionally
+ * FA_ERR_UNSUPPORTED for Sq > 32, FA_ERR_INVALID_ARG for Sq > Sk, a missing or
+ * short workspace, or o, lse or the workspace overlapping an input or each
+ * other. Returns FA_OK or a negative fa_status.
+ */
+int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+              int B, int H, int Sq, int Sk, int D, float scale, int mask_mode, int win_l,
+              int win_r, int dtype, void *workspace, int64_t workspace_bytes,
+              hipStream_t stream);
+
+/*
+ * fa_decode_workspace_bytes -- bytes of workspace fa_decode needs for these
+ * arguments on the current device (0 when one split suffices and none is
+ * needed). Returns the size, or the negative fa_status fa_decode would return
+ * for these arguments.
+ */
+int64_t fa_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l,
+                                  int win_r);
+
+/*
+ * fa_decode_flops -- algorithmic FLOPs of one fa_decode call: 4 * D * B * H *
+ * (visible (row, key) pairs), rows at positions Sk - Sq .. Sk - 1. Returns the
+ * count, or a negative fa_status.
+ */
+int64_t fa_decode_flops(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l, int win_r);
 
 /* fa_strerror -- static description of a status code (never NULL). */
 const char *fa_strerror(int status);

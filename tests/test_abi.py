@@ -30,7 +30,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert {"fa_fwd", "fa_fwd_flops", "fa_visible_pairs", "fa_strerror"} <= set(
+    assert {"fa_fwd", "fa_fwd_flops", "fa_visible_pairs", "fa_strerror", "fa_decode",
+            "fa_decode_workspace_bytes", "fa_decode_flops"} <= set(
         _declared_functions())
 
 

@@ -50,3 +50,19 @@ def test_lse_and_nonfinite():
     bad = r.copy()
     bad[0, 0] = np.nan
     assert not compare(_bits(bad, "f16"), None, r, None, "f16")["pass"]
+
+
+def test_bf16_mean_bound_scales_with_output_size():
+    """bf16 outputs of size ~0.5: one-ulp rounding flips on a fifth of the
+    elements stay inside the mean bound max(4e-4, 2^-9 mean|r|), on three
+    fifths they do not."""
+    rng = np.random.default_rng(5)
+    r = rng.uniform(0.5, 0.9, size=4000)
+    R = round_bf16(r)
+    ulp = ulp_bf16(R)
+    for share, ok in ((0.2, True), (0.6, False)):
+        flip = rng.random(r.size) < share
+        o = R + np.where(flip, ulp, 0.0)
+        o_bits = f32_to_bits(o.astype(np.float32), "bf16")
+        st = compare(o_bits, None, r, None, "bf16")
+        assert st["pass"] == ok, (share, st)

@@ -1,11 +1,13 @@
 """Fused attention forward for AMD Instinct MI355X (gfx950).
 
 A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
-``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops`` and ``fa_strerror`` carry
-the C names and arguments (marshalling only). ``forward`` is the convenience
-entry for torch tensors: torch supplies device memory and the stream; every
-step of the computation runs in the library's HIP kernels. There is no
-fallback: if the library is missing, importing this package raises.
+``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops``, ``fa_decode``,
+``fa_decode_workspace_bytes``, ``fa_decode_flops`` and ``fa_strerror`` carry
+the C names and arguments (marshalling only). ``forward`` and ``decode`` are
+the convenience entries for torch tensors: torch supplies device memory and
+the stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if the library is missing, importing this package
+raises.
 """
 import ctypes
 import math
@@ -14,7 +16,8 @@ import os
 __all__ = [
     "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
     "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
-    "fa_strerror", "forward", "lib_path", "library",
+    "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_strerror", "forward",
+    "decode", "lib_path", "library",
 ]
 
 FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_WINDOW = 0, 1, 2
@@ -50,6 +53,14 @@ def _load():
     lib.fa_visible_pairs.restype = ctypes.c_int64
     lib.fa_fwd_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     lib.fa_fwd_flops.restype = ctypes.c_int64
+    i64 = ctypes.c_int64
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci,
+                              ci, ci, vp, i64, vp]
+    lib.fa_decode.restype = ci
+    lib.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
+    lib.fa_decode_workspace_bytes.restype = i64
+    lib.fa_decode_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
+    lib.fa_decode_flops.restype = i64
     lib.fa_strerror.argtypes = [ci]
     lib.fa_strerror.restype = ctypes.c_char_p
     return lib
@@ -64,9 +75,9 @@ def library():
 
 
 class FaError(RuntimeError):
-    def __init__(self, status):
+    def __init__(self, status, fn="fa_fwd"):
         self.status = status
-        super().__init__(f"fa_fwd failed: {fa_strerror(status)} (status {status})")
+        super().__init__(f"{fn} failed: {fa_strerror(status)} (status {status})")
 
 
 # ---- the C functions, same names and arguments ------------------------------
@@ -83,6 +94,21 @@ def fa_visible_pairs(S, mask_mode, win_l=-1, win_r=-1):
 
 def fa_fwd_flops(B, H, S, D, mask_mode, win_l=-1, win_r=-1):
     return _lib.fa_fwd_flops(B, H, S, D, mask_mode, win_l, win_r)
+
+
+def fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
+              workspace, workspace_bytes, stream):
+    """Call ``fa_decode`` with raw device addresses (ints); return its status."""
+    return _lib.fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r,
+                          dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_workspace_bytes(B, H, Sq, Sk, D, mask_mode, win_l=-1, win_r=-1):
+    return _lib.fa_decode_workspace_bytes(B, H, Sq, Sk, D, mask_mode, win_l, win_r)
+
+
+def fa_decode_flops(B, H, Sq, Sk, D, mask_mode, win_l=-1, win_r=-1):
+    return _lib.fa_decode_flops(B, H, Sq, Sk, D, mask_mode, win_l, win_r)
 
 
 def fa_strerror(status):
@@ -143,4 +169,63 @@ def forward(q, k, v, *, scale=None, mask="full", window=(-1, -1), out=None, lse=
                         float(scale), _mask_code(mask), int(wl), int(wr), dtype, stream)
     if status != 0:
         raise FaError(status)
+    return out, lse
+
+
+def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse=None,
+           return_lse=True, workspace=None, stream=None):
+    """New query rows against a key/value cache on torch device tensors.
+
+    q: contiguous [B, H, Sq, D] (Sq <= 32); k, v: contiguous [B, H, Sk, D]
+    (Sk >= Sq), all float16 or all bfloat16 on one GPU. Query row i sits at
+    position Sk - Sq + i; ``mask``/``window`` as for ``forward``, applied at
+    that position. ``workspace``: optional uint8 device tensor of at least
+    ``fa_decode_workspace_bytes(...)`` bytes (allocated here when needed and
+    not given). Returns ``(o, lse)``.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, Sq, D] and k, v one [B, H, Sk, D] shape")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("q and k, v disagree on B, H or D")
+    Sk = k.shape[2]
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Sq) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor on q's device")
+    wl, wr = window
+    m = _mask_code(mask)
+    dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    with torch.cuda.device(q.device):
+        need = fa_decode_workspace_bytes(B, H, Sq, Sk, D, m, int(wl), int(wr))
+        if need < 0:
+            raise FaError(int(need), "fa_decode")
+        if workspace is None and need > 0:
+            workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        status = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr() if lse is not None else None, B, H, Sq, Sk, D,
+                           float(scale), m, int(wl), int(wr), dtype, ws_ptr, int(ws_bytes),
+                           stream)
+    if status != 0:
+        raise FaError(status, "fa_decode")
     return out, lse

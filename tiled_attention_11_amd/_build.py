@@ -1,4 +1,4 @@
-"""Compile the gfx950 attention-forward library (libfa.so) with hipcc.
+"""Compile the gfx950 attention library (libfa.so) with hipcc.
 
 Usage: ``python -m tiled_attention_11_amd._build`` or ``build()`` from Python.
 The library is built in-tree, next to this file.
@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_kernel.hip")]
+SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_kernel.hip"),
+           os.path.join(CSRC, "fa_decode.hip")]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

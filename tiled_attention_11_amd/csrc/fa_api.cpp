@@ -166,3 +166,153 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
     hipError_t err = fa::launch_fwd(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+// ---- new query rows against a key/value cache ---------------------------------
+
+namespace {
+
+// Everything fa_decode decides before launching: the visible tile range and
+// the split of it into per-workgroup ranges. Shared with the workspace query
+// so both agree on the number of splits.
+struct DecodePlan {
+    int win_lo, win_hi;
+    int t_first, t_last;
+    int tiles_per_split, nsplit;
+    int64_t ws_bytes;  // 0 when nsplit == 1
+    bool empty;        // B*H*Sq == 0: nothing to do
+};
+
+int plan_decode(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l, int win_r,
+                DecodePlan *pl) {
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || Sq > Sk) return FA_ERR_INVALID_ARG;
+    if (!window_of(mask_mode, win_l, win_r, &pl->win_lo, &pl->win_hi)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if (Sq > fa::kDecodeMaxRows) return FA_ERR_UNSUPPORTED;
+    pl->empty = (int64_t)B * H * Sq == 0;
+    pl->t_first = pl->t_last = 0;
+    pl->tiles_per_split = pl->nsplit = 1;
+    pl->ws_bytes = 0;
+    if (pl->empty) return FA_OK;
+    if ((uint64_t)Sk * D * 2 >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    // Keys visible from some row: row i sits at position Sk - Sq + i.
+    const int64_t pos0 = (int64_t)Sk - Sq;
+    int64_t lo, hi, lo2, hi2;
+    key_range(pos0, Sk, pl->win_lo, pl->win_hi, &lo, &hi);
+    key_range(pos0 + Sq - 1, Sk, pl->win_lo, pl->win_hi, &lo2, &hi2);
+    (void)hi;
+    (void)lo2;
+    pl->t_first = (int)(lo / fa::kDecodeBN);
+    pl->t_last = (int)(hi2 / fa::kDecodeBN);
+    const int nt = pl->t_last - pl->t_first + 1;
+    // Splits: about two workgroups (one wave each) per CU over all heads,
+    // never more than one per tile.
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu <= 0)
+        return FA_ERR_HIP;
+    const int64_t bh = (int64_t)B * H;
+    int64_t want = (2 * (int64_t)n_cu + bh - 1) / bh;
+    if (want > nt) want = nt;
+    if (want < 1) want = 1;
+    pl->tiles_per_split = (int)((nt + want - 1) / want);
+    pl->nsplit = (nt + pl->tiles_per_split - 1) / pl->tiles_per_split;
+    if (bh * pl->nsplit > (int64_t)INT32_MAX || bh * Sq > (int64_t)INT32_MAX)
+        return FA_ERR_TOO_LARGE;
+    if (pl->nsplit > 1) {
+        const __int128 ws = (__int128)bh * pl->nsplit * Sq * (D + 1) * 4;
+        if (ws > (__int128)INT64_MAX / 4) return FA_ERR_TOO_LARGE;
+        pl->ws_bytes = (int64_t)ws;
+    }
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int64_t fa_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int mask_mode,
+                                             int win_l, int win_r) {
+    DecodePlan pl;
+    const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, &pl);
+    return rc == FA_OK ? pl.ws_bytes : rc;
+}
+
+extern "C" int64_t fa_decode_flops(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l,
+                                   int win_r) {
+    int win_lo, win_hi;
+    if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || Sq > Sk || D <= 0 ||
+        !window_of(mask_mode, win_l, win_r, &win_lo, &win_hi))
+        return FA_ERR_INVALID_ARG;
+    int64_t pairs = 0;
+    for (int64_t i = 0; i < Sq; ++i) {
+        int64_t lo, hi;
+        key_range((int64_t)Sk - Sq + i, Sk, win_lo, win_hi, &lo, &hi);
+        if (hi >= lo) pairs += hi - lo + 1;
+    }
+    __int128 f = (__int128)4 * D * B * H * pairs;
+    if (f > (__int128)INT64_MAX) return FA_ERR_TOO_LARGE;
+    return (int64_t)f;
+}
+
+extern "C" int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int B, int H, int Sq, int Sk, int D, float scale, int mask_mode,
+                         int win_l, int win_r, int dtype, void *workspace,
+                         int64_t workspace_bytes, hipStream_t stream) {
+    // ---- scalar arguments and the plan (no HIP work queued before success) ----
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    DecodePlan pl;
+    const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, &pl);
+    if (rc != FA_OK) return rc;
+    if (pl.empty) return FA_OK;
+    if (workspace_bytes < 0) return FA_ERR_INVALID_ARG;
+
+    // ---- pointers ---------------------------------------------------------------
+    if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return FA_ERR_INVALID_ARG;
+    const uintptr_t pq = (uintptr_t)q, pk = (uintptr_t)k, pv = (uintptr_t)v, po = (uintptr_t)o,
+                    pl_ = (uintptr_t)lse, pw = (uintptr_t)workspace;
+    if ((pq | pk | pv | po) & 15u) return FA_ERR_ALIGNMENT;
+    if (lse && (pl_ & 3u)) return FA_ERR_ALIGNMENT;
+    if (pl.ws_bytes > 0 && (pw & 15u)) return FA_ERR_ALIGNMENT;
+    const uint64_t bh = (uint64_t)B * H;
+    const uint64_t qbytes = bh * Sq * D * 2, kvbytes = bh * Sk * D * 2, lbytes = bh * Sq * 4;
+    const uint64_t wbytes = (uint64_t)pl.ws_bytes;
+    // outputs and workspace must not overlap the inputs or each other
+    const uintptr_t outs[3] = {po, pl_, pw};
+    const uint64_t outn[3] = {qbytes, lse ? lbytes : 0, wbytes};
+    const uintptr_t ins[3] = {pq, pk, pv};
+    const uint64_t inn[3] = {qbytes, kvbytes, kvbytes};
+    for (int a = 0; a < 3; ++a) {
+        if (!outn[a]) continue;
+        for (int b = 0; b < 3; ++b)
+            if (overlaps(outs[a], outn[a], ins[b], inn[b])) return FA_ERR_INVALID_ARG;
+        for (int b = a + 1; b < 3; ++b)
+            if (outn[b] && overlaps(outs[a], outn[a], outs[b], outn[b])) return FA_ERR_INVALID_ARG;
+    }
+
+    // ---- launch -------------------------------------------------------------------
+    fa::DecodeParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.ws_o = pl.nsplit > 1 ? static_cast<float *>(workspace) : nullptr;
+    p.ws_lse = pl.nsplit > 1 ? static_cast<float *>(workspace) + bh * pl.nsplit * Sq * D : nullptr;
+    p.B = B;
+    p.H = H;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.pos0 = Sk - Sq;
+    p.win_lo = pl.win_lo;
+    p.win_hi = pl.win_hi;
+    p.c2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);  // as in fa_fwd
+    p.negate_q = scale < 0.0f;
+    p.t_first = pl.t_first;
+    p.t_last = pl.t_last;
+    p.tiles_per_split = pl.tiles_per_split;
+    p.nsplit = pl.nsplit;
+    hipError_t err = fa::launch_decode(p, D, dtype, stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+

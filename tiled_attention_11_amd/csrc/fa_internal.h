@@ -40,4 +40,30 @@ constexpr int kBlockM = 256;
 // Enqueue the kernel for head dimension D and dtype (0 fp16, 1 bf16).
 hipError_t launch_fwd(const FwdParams &p, int D, int dtype, hipStream_t stream);
 
+// ---- new query rows against a key/value cache ---------------------------------
+// Keys per tile of the cache kernel.
+constexpr int kDecodeBN = 32;
+// Query rows of one call: one wave's MFMA block.
+constexpr int kDecodeMaxRows = 32;
+
+struct DecodeParams {
+    const void *q;          // [B, H, Sq, D]
+    const void *k, *v;      // [B, H, Sk, D]
+    void *o;                // [B, H, Sq, D]
+    float *lse;             // [B, H, Sq] or nullptr
+    float *ws_o;            // nsplit > 1: partial outputs [B*H, nsplit, Sq, D]
+    float *ws_lse;          // nsplit > 1: partial LSEs [B*H, nsplit, Sq]
+    int B, H, Sq, Sk;
+    int pos0;               // Sk - Sq: position of query row 0 in the sequence
+    int win_lo, win_hi;     // as in FwdParams, relative to each row's position
+    float c2;
+    int negate_q;
+    int t_first, t_last;    // key tiles visible from some row (same for every head)
+    int tiles_per_split;    // a split covers this many consecutive tiles (the last may have fewer)
+    int nsplit;             // splits per head; 1 writes o and lse directly
+};
+
+// Enqueue the cache kernel (and, for nsplit > 1, the merge kernel).
+hipError_t launch_decode(const DecodeParams &p, int D, int dtype, hipStream_t stream);
+
 }  // namespace fa

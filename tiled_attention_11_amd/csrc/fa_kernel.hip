@@ -50,69 +50,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
-
-#define LDS __attribute__((address_space(3)))
+using namespace dev;
 
 constexpr int kWaves = 8;            // two groups of four, one wave of each per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveRows = 32;        // query rows per wave
 static_assert(kWaves * kWaveRows == kBlockM, "workgroup covers kBlockM rows");
-
-// Word 3 of a gfx9 buffer resource for raw (untyped, stride 0) access.
-constexpr int kBufferFlags = 0x00020000;
-
-// ---- element type traits --------------------------------------------------
-template <typename T> struct Elem;
-template <> struct Elem<_Float16> {
-    typedef f16x8 vec8;
-    typedef f16x2 vec2;
-    // The row sum adds the fp16-rounded probabilities (the P V operands), two
-    // per v_dot2 against (1, 1), in the MFMA phase; their rounding (relative
-    // 2^-12 at most) moves the LSE by under 2.5e-4.
-    static constexpr bool kSumRounded = true;
-    // acc + a.lo + a.hi for two packed fp16 values
-    static __device__ __forceinline__ float sum2(uint32_t a, float acc) {
-        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), one, acc, false);
-    }
-    static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    // two fp32 -> two fp16, round to nearest even, packed low|high
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        vec2 h = {(_Float16)a, (_Float16)b};
-        return __builtin_bit_cast(uint32_t, h);
-    }
-};
-template <> struct Elem<__bf16> {
-    typedef bf16x8 vec8;
-    typedef bf16x2 vec2;
-    // bf16 rounding (relative 2^-9) would move the LSE by up to 2e-3: the row
-    // sum adds the unrounded fp32 probabilities in the softmax instead.
-    static constexpr bool kSumRounded = false;
-    static __device__ __forceinline__ float sum2(uint32_t, float acc) { return acc; }
-    static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ uint32_t pack(float a, float b) {
-        vec2 h = {(__bf16)a, (__bf16)b};
-        return __builtin_bit_cast(uint32_t, h);
-    }
-};
 
 // ---- tile geometry per head dimension ---------------------------------------
 // D = 128: 64-key tiles; D = 64: 128-key tiles. Either way a K or V tile is
@@ -127,16 +76,8 @@ template <int D> struct Geom {
     static_assert(TILE_BYTES == 16384, "tile geometry");
     static_assert(DMA_PER_WAVE * kWaves * 1024 == TILE_BYTES, "DMA split");
 
-    // Physical 16-byte chunk of logical chunk q in K row r: the 16 rows read
-    // together by one 16-lane group land on 16 different 4-bank groups.
-    static __device__ __forceinline__ int kchunk(int q, int r) {
-        return D == 128 ? (q ^ (r & 15)) : (q ^ ((r >> 1) & 7));
-    }
-    // Physical chunk of logical chunk q in V row r: the 4 rows x 64 bytes read
-    // by 32 lanes of a transposing load land in 4 different 64-byte segments.
-    static __device__ __forceinline__ int vchunk(int q, int r) {
-        return D == 128 ? (q ^ ((r & 3) << 2)) : (q ^ (((r >> 1) & 1) << 2));
-    }
+    static __device__ __forceinline__ int kchunk(int q, int r) { return dev::kchunk<D>(q, r); }
+    static __device__ __forceinline__ int vchunk(int q, int r) { return dev::vchunk<D>(q, r); }
 };
 
 template <typename T, int D>
@@ -176,35 +117,6 @@ struct Kernel {
     // MFMAs between an LDS operand read and its use in the MFMA phase.
     static constexpr int kDist = 8;
 
-    // Materialise a value here: the compiler may not move its computation past
-    // this point (it would otherwise sink the softmax of one phase into the
-    // next, or the MFMAs of one phase past the barrier that ends it).
-    static __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
-    static __device__ __forceinline__ void pin(f32x16 &x) { asm volatile("" : "+v"(x)); }
-    template <int N> static __device__ __forceinline__ void pin(f32x16 (&x)[N]) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) pin(x[n]);
-    }
-    template <int N, int M> static __device__ __forceinline__ void pin(uint32_t (&x)[N][M]) {
-#pragma unroll
-        for (int n = 0; n < N; ++n)
-#pragma unroll
-            for (int m = 0; m < M; ++m) asm volatile("" : "+v"(x[n][m]));
-    }
-
-    static __device__ __forceinline__ float max_with_partner(float x) {
-        const uint32_t u = __builtin_bit_cast(uint32_t, x);
-        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]),
-                     __builtin_bit_cast(float, (uint32_t)r[1]));
-    }
-    static __device__ __forceinline__ float sum_with_partner(float x) {
-        const uint32_t u = __builtin_bit_cast(uint32_t, x);
-        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        return __builtin_bit_cast(float, (uint32_t)r[0]) +
-               __builtin_bit_cast(float, (uint32_t)r[1]);
-    }
-
     static __device__ __forceinline__ void make_addr(Addr &ad, int wave, int lane) {
         const int l32 = lane & 31, g = lane >> 5;
         // DMA block b = DMA_PER_WAVE * wave + i fills tile rows
@@ -231,33 +143,6 @@ struct Kernel {
             const int col = 32 * db + 16 * h + 4 * (q & 3);
             ad.v[db] = vrow * G::RB + G::vchunk(col >> 3, vrow) * 16 + (col & 7) * 2;
         }
-    }
-
-    // Raw buffer resource (base, num_records bytes, stride 0) as 4 SGPRs.
-    static __device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
-        const uint64_t a = (uint64_t)base;
-        return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes,
-                     kBufferFlags};
-    }
-
-    // 16 bytes per lane from the buffer at voffset straight into LDS at
-    // lds_base + 16 * lane (buffer_load_dwordx4 ... lds; offsets outside the
-    // resource read as zero). Issued from inline assembly so that the compiler
-    // does not guard every later LDS read with a wait for this load: the
-    // kernel orders DMA and LDS reads itself (vmcnt wait + barrier per tile).
-    // M0 carries the LDS base and is restored, with the one wait state the
-    // hardware needs between an SALU write of M0 and its use by the load.
-    static __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
-        uint32_t saved;
-        asm volatile(
-            "s_mov_b32 %0, m0\n\t"
-            "s_mov_b32 m0, %1\n\t"
-            "s_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved)
-            : "s"(lds_base), "v"(voffset), "s"(rsrc)
-            : "memory");
     }
 
     // Stream one K or V tile (rows k0 .. k0 + BN - 1 of the head at `h`) into
