@@ -6,6 +6,10 @@ Prints one JSON line: TFLOP/s (4*D*B*H*visible pairs per call / average
 kernel time), the roofline of the kernel against the dense fp16 MFMA peak,
 and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
+With ``--workload decode_*`` one step is one fa_decode call (new query rows
+against a key/value cache, HBM-bound): the line reports GB/s of algorithmic
+bytes against the 8 TB/s HBM peak instead.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds T]
 """
 import argparse
@@ -22,28 +26,34 @@ sys.path.insert(0, ROOT)
 
 # MI355X dense fp16/bf16 MFMA peak: 256 CUs x 4096 FLOP/clk/CU x 2.4 GHz.
 PEAK_FP16_TFLOPS = 2516.6
+# MI355X HBM3E peak bandwidth.
+PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["tiled_attention_11_amd/csrc/fa_kernel.hip",
-                  "tiled_attention_11_amd/csrc/fa_internal.h"]
+                  "tiled_attention_11_amd/csrc/fa_internal.h",
+                  "tiled_attention_11_amd/csrc/fa_device.h"]
+DECODE_SOURCES = ["tiled_attention_11_amd/csrc/fa_decode.hip",
+                  "tiled_attention_11_amd/csrc/fa_internal.h",
+                  "tiled_attention_11_amd/csrc/fa_device.h"]
 
 
-def kernel_sha256():
+def kernel_sha256(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def counted_traffic(workload):
+def counted_traffic(workload, prefix="fa_fwd", sources=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fa_fwd_{workload}.pmc.md")
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload}.pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not sha or not val or sha.group(1) != kernel_sha256():
+    if not sha or not val or sha.group(1) != kernel_sha256(sources):
         return None
     return int(val.group(1))
 
@@ -100,6 +110,135 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, seconds):
     return base, parity
 
 
+def decode_bytes(w):
+    """Algorithmic HBM bytes of one fa_decode call: q read, the visible part of
+    the cache (k and v) read once, o and lse written."""
+    B, H, Sq, Sk, D = w["B"], w["H"], w["Sq"], w["Sk"], w["D"]
+    lo_hi = []
+    for i in (Sk - Sq, Sk - 1):  # positions of the first and the last new row
+        lo = 0 if w["mask"] != "window" or w["window"][0] < 0 else max(0, i - w["window"][0])
+        hi = Sk - 1 if w["mask"] == "full" or (w["mask"] == "window" and w["window"][1] < 0) else \
+            min(Sk - 1, i + (0 if w["mask"] == "causal" else w["window"][1]))
+        lo_hi.append((lo, hi))
+    keys = lo_hi[1][1] - lo_hi[0][0] + 1
+    return B * H * (2 * Sq * D * 2 + 2 * keys * D * 2 + Sq * 4)
+
+
+def bench_decode(args, name):
+    import numpy as np
+    import torch
+
+    import synth
+    import tiled_attention_11_amd as fa
+
+    w = synth.DECODE_WORKLOADS[name]
+    B, H, Sq, Sk, D, dtype = w["B"], w["H"], w["Sq"], w["Sk"], w["D"], w["dtype"]
+    wl, wr = w["window"]
+    m = fa._mask_code(w["mask"])
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v = synth.decode_inputs(name)
+    tq, tk, tv = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
+    out = torch.empty_like(tq)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    need = fa.fa_decode_workspace_bytes(B, H, Sq, Sk, D, m, wl, wr)
+    ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s, workspace "
+          f"{need} B", file=sys.stderr, flush=True)
+
+    def step():
+        fa.decode(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
+                  lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]) * 1e-3
+    avg_s = evs[0].elapsed_time(evs[-1]) * 1e-3 / args.steps
+    print(f"[bench] timed {args.steps} steps: avg {avg_s * 1e6:.1f} us, median "
+          f"{np.median(per) * 1e6:.1f} us", file=sys.stderr, flush=True)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+
+    nbytes = decode_bytes(w)
+    gbs = nbytes / avg_s / 1e9
+    flops = fa.fa_decode_flops(B, H, Sq, Sk, D, m, wl, wr)
+    result = {
+        "metric": "cache attention (new rows against a key/value cache) HBM GB/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(avg_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{name}: B={B} H={H} Sq={Sq} Sk={Sk} D={D} {dtype} {w['mask']}"
+                         f" scale={w['scale']:.6g}"),
+            "B": B, "H": H, "Sq": Sq, "Sk": Sk, "D": D, "mask": w["mask"], "window": [wl, wr],
+            "bytes_per_step": nbytes, "flops_per_step": flops, "workspace_bytes": int(need),
+        },
+        "tflops": round(flops / avg_s / 1e12, 3),
+        "median_launch_us": round(float(np.median(per)) * 1e6, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": counted_traffic(name, "fa", DECODE_SOURCES),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        from tests.parity import compare
+        orc = oracle.load()
+        o_bits = out.cpu().view(torch.int16).numpy().view(np.uint16)
+        lse_h = lse.cpu().numpy()
+        # whole heads, in order, until the time budget is spent
+        heads, t_used, pairs = 0, 0.0, 0
+        stats = []
+        per_head = flops // (4 * D * B * H)
+        while heads < B * H and t_used < args.cpu_seconds:
+            b, h = divmod(heads, H)
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            t0 = time.perf_counter()
+            o_ref, lse_ref = orc.attention_kv(q[sl], k[sl], v[sl], dtype, w["scale"], w["mask"],
+                                              (wl, wr))
+            t_used += time.perf_counter() - t0
+            stats.append(compare(o_bits[sl], lse_h[sl], o_ref, lse_ref, dtype))
+            heads += 1
+            pairs += per_head
+        head_bytes = nbytes // (B * H)
+        result["cpu_baseline"] = {
+            "value": round(heads * head_bytes / t_used / 1e9, 4), "unit": "GB/s",
+            "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"{heads} whole heads of the same workload ({heads * head_bytes} bytes, "
+                      f"{pairs} visible pairs), {t_used:.2f} s wall, fp64",
+        }
+        result["parity_sample"] = {"heads": heads, "pass": all(s["pass"] for s in stats),
+                                   "max_abs": max(s["max_abs"] for s in stats),
+                                   "lse_max_abs": max(s.get("lse_max_abs", 0.0) for s in stats)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +266,8 @@ def main():
     import tiled_attention_11_amd as fa
 
     name = args.workload or synth.HEADLINE
+    if name in synth.DECODE_WORKLOADS:
+        return bench_decode(args, name)
     w = synth.WORKLOADS[name]
     B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
     wl, wr = w["window"]

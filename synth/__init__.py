@@ -45,6 +45,20 @@ WORKLOADS = {
 
 HEADLINE = "b4h32s4096_causal"
 
+# New query rows against a key/value cache (incremental decoding): Sq rows at
+# the end of sequences whose first Sk positions the cache holds. The NPU
+# optimisation page's hands-on section runs batch 1, 32 heads, D = 128 against
+# a cache; these stand in for a serving step at long context (one new token,
+# and 16 new tokens as in speculative decoding or chunked prefill).
+DECODE_WORKLOADS = {
+    "decode_b1h32_q1_k8192":   dict(B=1, H=32, Sq=1, Sk=8192, D=128, dtype="f16",
+                                    mask="causal", window=(-1, -1), scale=128 ** -0.5, seed=6),
+    "decode_b4h32_q1_k16384":  dict(B=4, H=32, Sq=1, Sk=16384, D=128, dtype="f16",
+                                    mask="causal", window=(-1, -1), scale=128 ** -0.5, seed=7),
+    "decode_b4h32_q16_k16384": dict(B=4, H=32, Sq=16, Sk=16384, D=128, dtype="f16",
+                                    mask="causal", window=(-1, -1), scale=128 ** -0.5, seed=8),
+}
+
 
 def f32_to_bits(x, dtype):
     """Round fp32 values once to ``dtype`` ('f16' or 'bf16'); return uint16 bits."""
@@ -74,6 +88,22 @@ def make_qkv(B, H, S, D, dtype, seed, outlier_frac=0.0, outlier_scale=20.0):
                     rows = rng.choice(S, size=n, replace=False)
                     k[b, h, rows, :] *= np.float32(outlier_scale)
     return f32_to_bits(q, dtype), f32_to_bits(k, dtype), f32_to_bits(v, dtype)
+
+
+def make_decode_qkv(B, H, Sq, Sk, D, dtype, seed):
+    """q [B,H,Sq,D] and the cache k, v [B,H,Sk,D]: standard normal fp32 drawn in
+    the order q, k, v from one generator, each rounded once to ``dtype``."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Sq, D), dtype=np.float32)
+    k = rng.standard_normal((B, H, Sk, D), dtype=np.float32)
+    v = rng.standard_normal((B, H, Sk, D), dtype=np.float32)
+    return f32_to_bits(q, dtype), f32_to_bits(k, dtype), f32_to_bits(v, dtype)
+
+
+def decode_inputs(name):
+    """(q, k, v) bit arrays for a named cache workload."""
+    w = DECODE_WORKLOADS[name]
+    return make_decode_qkv(w["B"], w["H"], w["Sq"], w["Sk"], w["D"], w["dtype"], w["seed"])
 
 
 def workload_inputs(name):
