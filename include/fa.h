@@ -165,6 +165,43 @@ int64_t fa_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int mask_
                                   int win_r);
 
 /*
+ * fa_decode_paged -- fa_decode over a paged key/value cache (serving layout).
+ * The cached keys and values of all sequences live in page pools
+ * k_pages, v_pages: [num_pages, page_size, H, D] of `dtype`; key j of sequence b
+ * is row j % page_size of page block_table[b * max_pages + j / page_size], and
+ * sequence b caches seq_lens[b] keys (its new rows are its last Sq positions).
+ * Defining passage: as fa_decode; the paged layout is the serving form of the
+ * same cache ("optimisation 4: KV-cache reuse" keeps the cache across steps).
+ *
+ * block_table  device pointer, int32 [B, max_pages]; read only. Entries past a
+ *              sequence's pages are not read. An entry outside [0, num_pages)
+ *              makes that page's keys read as zero (nothing outside the pools
+ *              is touched).
+ * seq_lens     device pointer, int32 [B]; read only; each value is clamped to
+ *              [0, max_seq_len]. A row at a negative position (seq_lens[b] < Sq)
+ *              sees no key: its output is 0 and its LSE -inf.
+ * max_seq_len  host-side bound on seq_lens (sizes the split); Sq <= max_seq_len
+ *              <= max_pages * page_size.
+ * num_pages    pages in each pool (>= 1); page_size a positive multiple of 32.
+ * Other arguments, the workspace (size from fa_decode_paged_workspace_bytes) and
+ * the error rules as fa_decode; FA_ERR_UNSUPPORTED for a page_size that is not a
+ * positive multiple of 32, FA_ERR_ALIGNMENT for block_table or seq_lens not
+ * 4-byte aligned.
+ */
+int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, void *o, float *lse,
+                    const int32_t *block_table, const int32_t *seq_lens, int B, int H, int Sq,
+                    int max_seq_len, int D, int num_pages, int page_size, int max_pages,
+                    float scale, int mask_mode, int win_l, int win_r, int dtype,
+                    void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_decode_paged_workspace_bytes -- workspace fa_decode_paged needs on the
+ * current device for these arguments (0 if none), or a negative fa_status.
+ */
+int64_t fa_decode_paged_workspace_bytes(int B, int H, int Sq, int max_seq_len, int D,
+                                        int mask_mode, int win_l, int win_r);
+
+/*
  * fa_decode_flops -- algorithmic FLOPs of one fa_decode call: 4 * D * B * H *
  * (visible (row, key) pairs), rows at positions Sk - Sq .. Sk - 1. Returns the
  * count, or a negative fa_status.

@@ -63,3 +63,26 @@ def test_flops_count_visible_pairs_at_the_rows_positions(orc, Sq, Sk, mask, wind
 def test_flops_rejects_bad_arguments():
     assert fa.fa_decode_flops(1, 1, 5, 4, 64, 1, -1, -1) == INVALID
     assert fa.fa_decode_flops(1, 1, 2, 4, 64, 9, -1, -1) == INVALID
+
+
+def call_paged(B=2, H=3, Sq=4, max_seq=100, D=128, num_pages=8, page_size=64, max_pages=2,
+               mask=1, dtype=0):
+    return fa.fa_decode_paged(Q, K, V, O, L, W, W + 4096, B, H, Sq, max_seq, D, num_pages,
+                              page_size, max_pages, 0.1, mask, -1, -1, dtype, W + 8192, 1 << 30,
+                              None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=0), UNSUPPORTED), (dict(page_size=16), UNSUPPORTED),
+    (dict(page_size=48), UNSUPPORTED), (dict(page_size=-32), UNSUPPORTED),
+    (dict(num_pages=0), INVALID), (dict(max_pages=0), INVALID),
+    (dict(max_pages=1, page_size=64, max_seq=100), INVALID),
+    (dict(Sq=5, max_seq=4), INVALID), (dict(Sq=33), UNSUPPORTED), (dict(D=96), UNSUPPORTED),
+    (dict(dtype=3), INVALID), (dict(mask=5), INVALID),
+])
+def test_paged_rejected_before_launch(kw, code):
+    assert call_paged(**kw) == code
+
+
+def test_paged_empty_problem_is_a_no_op():
+    assert call_paged(B=0) == OK and call_paged(Sq=0) == OK

@@ -130,3 +130,114 @@ def test_decode_long_cache_sampled_heads(orc, dtype):
                                           "causal")
         st = compare(o_bits[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], o_ref, lse_ref, dtype)
         assert st["pass"], (b, h, st)
+
+
+# ---------------------------------------------------------------------------
+# paged cache: pools [num_pages, page_size, H, D], a block table per sequence,
+# per-sequence lengths; the oracle sees each sequence's contiguous cache
+
+def build_pages(k, v, seq_lens, page_size, rng, extra_pages=3):
+    """Scatter contiguous caches k, v [B, H, Sk, D] into randomly placed pages;
+    unused table entries hold -1."""
+    B, H, Sk, D = k.shape
+    need = [(L + page_size - 1) // page_size for L in seq_lens]
+    max_pages = max(max(need), 1) + 1
+    num_pages = sum(need) + extra_pages
+    order = rng.permutation(num_pages)
+    kp = np.zeros((num_pages, page_size, H, D), np.uint16)
+    vp = np.zeros_like(kp)
+    table = np.full((B, max_pages), -1, np.int32)
+    nxt = 0
+    for b, L in enumerate(seq_lens):
+        for j in range(need[b]):
+            pg = int(order[nxt])
+            nxt += 1
+            table[b, j] = pg
+            lo, hi = j * page_size, min(L, (j + 1) * page_size)
+            kp[pg, :hi - lo] = k[b, :, lo:hi, :].transpose(1, 0, 2)
+            vp[pg, :hi - lo] = v[b, :, lo:hi, :].transpose(1, 0, 2)
+    return kp, vp, table
+
+
+def run_paged(q, kp, vp, table, seq_lens, max_seq, dtype, scale, mask, window=(-1, -1)):
+    tq, tkp, tvp = (to_device(x, dtype) for x in (q, kp, vp))
+    tt = torch.from_numpy(table).cuda()
+    tl = torch.tensor(seq_lens, dtype=torch.int32, device="cuda")
+    o, lse = fa.decode_paged(tq, tkp, tvp, tt, tl, max_seq, scale=scale, mask=mask,
+                             window=window)
+    torch.cuda.synchronize()
+    return to_bits(o), lse.cpu().numpy()
+
+
+PAGED = [  # B, H, Sq, seq_lens, D, page_size
+    (3, 2, 1, [37, 300, 1000], 128, 32),
+    (2, 4, 4, [4, 2049], 128, 64),
+    (4, 1, 16, [16, 100, 513, 4096], 64, 256),
+    (2, 2, 32, [700, 33], 128, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("case", PAGED, ids=lambda c: f"B{c[0]}H{c[1]}q{c[2]}d{c[4]}p{c[5]}")
+@pytest.mark.parametrize("mask,window", [("causal", (-1, -1)), ("full", (-1, -1)),
+                                         ("window", (200, 0)), ("window", (40, 5))], ids=str)
+def test_paged_parity(orc, dtype, case, mask, window):
+    B, H, Sq, seq_lens, D, ps = case
+    max_seq = max(seq_lens)
+    seed = 900 + Sq + D + ps
+    say("paged", dtype, case, mask, window, "seed", seed)
+    rng = np.random.default_rng(seed)
+    q, k, v = make(B, H, Sq, max_seq, D, dtype, seed)
+    kp, vp, table = build_pages(k, v, seq_lens, ps, rng)
+    o_bits, lse = run_paged(q, kp, vp, table, seq_lens, max_seq, dtype, 0.1, mask, window)
+    for b, L in enumerate(seq_lens):
+        o_ref, lse_ref = orc.attention_kv(q[b:b + 1], k[b:b + 1, :, :L], v[b:b + 1, :, :L],
+                                          dtype, 0.1, mask, window)
+        st = compare(o_bits[b:b + 1], lse[b:b + 1], o_ref, lse_ref, dtype)
+        assert st["pass"], (b, L, st)
+
+
+def test_paged_short_sequence_rows_see_nothing(orc):
+    """seq_len < Sq: rows at negative positions get O = 0 and LSE = -inf; the
+    others attend over the keys they can see."""
+    B, H, Sq, D, ps = 1, 2, 8, 64, 32
+    seq_lens = [5]
+    say("paged short", B, H, Sq, seq_lens)
+    q, k, v = make(B, H, Sq, 40, D, "f16", seed=77)
+    kp, vp, table = build_pages(k, v, seq_lens, ps, np.random.default_rng(1))
+    o_bits, lse = run_paged(q, kp, vp, table, seq_lens, 40, "f16", 0.2, "causal")
+    n_dead = Sq - seq_lens[0]
+    assert np.all(o_bits[:, :, :n_dead] == 0) and np.all(lse[:, :, :n_dead] == -np.inf)
+    o_ref, lse_ref = orc.attention_kv(q[:, :, n_dead:], k[:, :, :5], v[:, :, :5], "f16", 0.2,
+                                      "causal")
+    assert compare(o_bits[:, :, n_dead:], lse[:, :, n_dead:], o_ref, lse_ref, "f16")["pass"]
+
+
+def test_paged_bad_page_index_reads_zero_keys(orc):
+    """A table entry outside the pool makes that page's keys and values zero."""
+    B, H, Sq, D, ps = 1, 2, 2, 128, 32
+    seq_lens = [96]
+    say("paged bad page", B, H, Sq, seq_lens)
+    q, k, v = make(B, H, Sq, 96, D, "f16", seed=78)
+    kp, vp, table = build_pages(k, v, seq_lens, ps, np.random.default_rng(2))
+    table[0, 1] = kp.shape[0] + 5  # the second page: keys 32 .. 63
+    o_bits, lse = run_paged(q, kp, vp, table, seq_lens, 96, "f16", 0.1, "full")
+    k0, v0 = k.copy(), v.copy()
+    k0[:, :, 32:64] = 0
+    v0[:, :, 32:64] = 0
+    o_ref, lse_ref = orc.attention_kv(q, k0, v0, "f16", 0.1, "full")
+    assert compare(o_bits, lse, o_ref, lse_ref, "f16")["pass"]
+
+
+def test_paged_equals_contiguous_bitwise():
+    """One sequence whose pages are in order is the contiguous cache: same
+    kernel, same tiles, so the same bits."""
+    B, H, Sq, Sk, D, ps = 1, 1, 3, 512, 128, 64
+    say("paged vs contiguous", B, H, Sq, Sk)
+    q, k, v = make(B, H, Sq, Sk, D, "bf16", seed=79)
+    kp = k[0].transpose(1, 0, 2).reshape(Sk // ps, ps, H, D).copy()
+    vp = v[0].transpose(1, 0, 2).reshape(Sk // ps, ps, H, D).copy()
+    table = np.arange(Sk // ps, dtype=np.int32)[None, :]
+    a = run_paged(q, kp, vp, table, [Sk], Sk, "bf16", 0.1, "causal")
+    b = run(q, k, v, "bf16", 0.1, "causal")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -2,8 +2,9 @@
 
 A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
 ``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops``, ``fa_decode``,
-``fa_decode_workspace_bytes``, ``fa_decode_flops`` and ``fa_strerror`` carry
-the C names and arguments (marshalling only). ``forward`` and ``decode`` are
+``fa_decode_workspace_bytes``, ``fa_decode_flops``, ``fa_decode_paged``,
+``fa_decode_paged_workspace_bytes`` and ``fa_strerror`` carry the C names and
+arguments (marshalling only). ``forward``, ``decode`` and ``decode_paged`` are
 the convenience entries for torch tensors: torch supplies device memory and
 the stream; every step of the computation runs in the library's HIP kernels.
 There is no fallback: if the library is missing, importing this package
@@ -16,8 +17,9 @@ import os
 __all__ = [
     "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
     "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
-    "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_strerror", "forward",
-    "decode", "lib_path", "library",
+    "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
+    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "decode", "decode_paged",
+    "lib_path", "library",
 ]
 
 FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_WINDOW = 0, 1, 2
@@ -59,6 +61,11 @@ def _load():
     lib.fa_decode.restype = ci
     lib.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     lib.fa_decode_workspace_bytes.restype = i64
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
+                                    ctypes.c_float, ci, ci, ci, ci, vp, i64, vp]
+    lib.fa_decode_paged.restype = ci
+    lib.fa_decode_paged_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
+    lib.fa_decode_paged_workspace_bytes.restype = i64
     lib.fa_decode_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     lib.fa_decode_flops.restype = i64
     lib.fa_strerror.argtypes = [ci]
@@ -109,6 +116,21 @@ def fa_decode_workspace_bytes(B, H, Sq, Sk, D, mask_mode, win_l=-1, win_r=-1):
 
 def fa_decode_flops(B, H, Sq, Sk, D, mask_mode, win_l=-1, win_r=-1):
     return _lib.fa_decode_flops(B, H, Sq, Sk, D, mask_mode, win_l, win_r)
+
+
+def fa_decode_paged(q, k_pages, v_pages, o, lse, block_table, seq_lens, B, H, Sq, max_seq_len,
+                    D, num_pages, page_size, max_pages, scale, mask_mode, win_l, win_r, dtype,
+                    workspace, workspace_bytes, stream):
+    """Call ``fa_decode_paged`` with raw device addresses (ints); return its status."""
+    return _lib.fa_decode_paged(q, k_pages, v_pages, o, lse, block_table, seq_lens, B, H, Sq,
+                                max_seq_len, D, num_pages, page_size, max_pages, scale,
+                                mask_mode, win_l, win_r, dtype, workspace, workspace_bytes,
+                                stream)
+
+
+def fa_decode_paged_workspace_bytes(B, H, Sq, max_seq_len, D, mask_mode, win_l=-1, win_r=-1):
+    return _lib.fa_decode_paged_workspace_bytes(B, H, Sq, max_seq_len, D, mask_mode, win_l,
+                                                win_r)
 
 
 def fa_strerror(status):
@@ -228,4 +250,64 @@ def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse
                            stream)
     if status != 0:
         raise FaError(status, "fa_decode")
+    return out, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, max_seq_len, *, scale=None,
+                 mask="causal", window=(-1, -1), out=None, lse=None, return_lse=True,
+                 workspace=None, stream=None):
+    """``decode`` over a paged cache on torch device tensors.
+
+    q: contiguous [B, H, Sq, D]; k_pages, v_pages: contiguous
+    [num_pages, page_size, H, D] (page_size a multiple of 32); block_table:
+    int32 [B, max_pages]; seq_lens: int32 [B] (each >= Sq, <= max_seq_len,
+    the host-side bound). Returns ``(o, lse)``.
+    """
+    import torch
+
+    if q.dim() != 4 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape:
+        raise ValueError("q must be [B, H, Sq, D] and the pools one [P, page, H, D] shape")
+    B, H, Sq, D = q.shape
+    num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
+    if k_pages.shape[2] != H or k_pages.shape[3] != D:
+        raise ValueError("the pools disagree with q on H or D")
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32 [B, max_pages]")
+    if seq_lens.shape != (B,) or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32 [B]")
+    max_pages = block_table.shape[1]
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous and on q's device")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_pages.dtype != q.dtype \
+            or v_pages.dtype != q.dtype:
+        raise ValueError("q and the pools must all be float16 or all bfloat16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    wl, wr = window
+    m = _mask_code(mask)
+    dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    with torch.cuda.device(q.device):
+        need = fa_decode_paged_workspace_bytes(B, H, Sq, int(max_seq_len), D, m, int(wl), int(wr))
+        if need < 0:
+            raise FaError(int(need), "fa_decode_paged")
+        if workspace is None and need > 0:
+            workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        status = fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                 out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                 block_table.data_ptr(), seq_lens.data_ptr(), B, H, Sq,
+                                 int(max_seq_len), D, num_pages, page_size, max_pages,
+                                 float(scale), m, int(wl), int(wr), dtype, ws_ptr, int(ws_bytes),
+                                 stream)
+    if status != 0:
+        raise FaError(status, "fa_decode_paged")
     return out, lse

@@ -7,6 +7,7 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -171,39 +172,46 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
 
 namespace {
 
-// Everything fa_decode decides before launching: the visible tile range and
-// the split of it into per-workgroup ranges. Shared with the workspace query
-// so both agree on the number of splits.
+// Everything fa_decode decides before launching: the split of the visible
+// tile range into per-workgroup ranges. Shared with the workspace queries so
+// both agree on the number of splits.
 struct DecodePlan {
     int win_lo, win_hi;
-    int t_first, t_last;
     int tiles_per_split, nsplit;
     int64_t ws_bytes;  // 0 when nsplit == 1
     bool empty;        // B*H*Sq == 0: nothing to do
 };
 
+// Sk is the cache length (paged: the largest any sequence may have). With
+// `paged` the sequences' lengths are unknown here, so the split is planned
+// over the most tiles any sequence's rows can see.
 int plan_decode(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l, int win_r,
-                DecodePlan *pl) {
+                bool paged, DecodePlan *pl) {
     if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || Sq > Sk) return FA_ERR_INVALID_ARG;
     if (!window_of(mask_mode, win_l, win_r, &pl->win_lo, &pl->win_hi)) return FA_ERR_INVALID_ARG;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
     if (Sq > fa::kDecodeMaxRows) return FA_ERR_UNSUPPORTED;
     pl->empty = (int64_t)B * H * Sq == 0;
-    pl->t_first = pl->t_last = 0;
     pl->tiles_per_split = pl->nsplit = 1;
     pl->ws_bytes = 0;
     if (pl->empty) return FA_OK;
     if ((uint64_t)Sk * D * 2 >= (1ull << 31)) return FA_ERR_TOO_LARGE;
-    // Keys visible from some row: row i sits at position Sk - Sq + i.
-    const int64_t pos0 = (int64_t)Sk - Sq;
-    int64_t lo, hi, lo2, hi2;
-    key_range(pos0, Sk, pl->win_lo, pl->win_hi, &lo, &hi);
-    key_range(pos0 + Sq - 1, Sk, pl->win_lo, pl->win_hi, &lo2, &hi2);
-    (void)hi;
-    (void)lo2;
-    pl->t_first = (int)(lo / fa::kDecodeBN);
-    pl->t_last = (int)(hi2 / fa::kDecodeBN);
-    const int nt = pl->t_last - pl->t_first + 1;
+    int64_t nt;  // tiles the rows of one sequence can see
+    if (!paged) {
+        // rows at positions Sk - Sq .. Sk - 1
+        int64_t lo, hi, lo2, hi2;
+        key_range((int64_t)Sk - Sq, Sk, pl->win_lo, pl->win_hi, &lo, &hi);
+        key_range((int64_t)Sk - 1, Sk, pl->win_lo, pl->win_hi, &lo2, &hi2);
+        (void)hi;
+        (void)lo2;
+        nt = hi2 / fa::kDecodeBN - lo / fa::kDecodeBN + 1;
+    } else {
+        // a window spans at most Sq - 1 + win_lo + win_hi + 1 keys, plus one
+        // partial tile at each end
+        const int64_t span = (int64_t)Sq + pl->win_lo + pl->win_hi;
+        const int64_t all = ((int64_t)Sk + fa::kDecodeBN - 1) / fa::kDecodeBN;
+        nt = std::min<int64_t>(all, span / fa::kDecodeBN + 2);
+    }
     // Splits: about two workgroups (one wave each) per CU over all heads,
     // never more than one per tile.
     int dev = 0, n_cu = 0;
@@ -216,7 +224,7 @@ int plan_decode(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l, i
     if (want > nt) want = nt;
     if (want < 1) want = 1;
     pl->tiles_per_split = (int)((nt + want - 1) / want);
-    pl->nsplit = (nt + pl->tiles_per_split - 1) / pl->tiles_per_split;
+    pl->nsplit = (int)((nt + pl->tiles_per_split - 1) / pl->tiles_per_split);
     if (bh * pl->nsplit > (int64_t)INT32_MAX || bh * Sq > (int64_t)INT32_MAX)
         return FA_ERR_TOO_LARGE;
     if (pl->nsplit > 1) {
@@ -232,7 +240,14 @@ int plan_decode(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l, i
 extern "C" int64_t fa_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int mask_mode,
                                              int win_l, int win_r) {
     DecodePlan pl;
-    const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, &pl);
+    const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, false, &pl);
+    return rc == FA_OK ? pl.ws_bytes : rc;
+}
+
+extern "C" int64_t fa_decode_paged_workspace_bytes(int B, int H, int Sq, int max_seq_len, int D,
+                                                   int mask_mode, int win_l, int win_r) {
+    DecodePlan pl;
+    const int rc = plan_decode(B, H, Sq, max_seq_len, D, mask_mode, win_l, win_r, true, &pl);
     return rc == FA_OK ? pl.ws_bytes : rc;
 }
 
@@ -253,39 +268,57 @@ extern "C" int64_t fa_decode_flops(int B, int H, int Sq, int Sk, int D, int mask
     return (int64_t)f;
 }
 
-extern "C" int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
-                         int B, int H, int Sq, int Sk, int D, float scale, int mask_mode,
-                         int win_l, int win_r, int dtype, void *workspace,
-                         int64_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Checks and launch shared by the contiguous and the paged cache entry points.
+// kv_bytes: bytes of one of k, v (the pool when paged).
+int decode_common(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                  int Sq, int Sk, int D, float scale, int mask_mode, int win_l, int win_r,
+                  int dtype, void *workspace, int64_t workspace_bytes, hipStream_t stream,
+                  const int32_t *block_table, const int32_t *seq_lens, int num_pages,
+                  int page_size, int max_pages) {
     // ---- scalar arguments and the plan (no HIP work queued before success) ----
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    const bool paged = block_table != nullptr || seq_lens != nullptr || page_size != 0;
+    if (paged) {
+        if (page_size <= 0 || page_size % fa::kDecodeBN != 0) return FA_ERR_UNSUPPORTED;
+        if (num_pages < 1 || max_pages < 1) return FA_ERR_INVALID_ARG;
+        if ((int64_t)max_pages * page_size < Sk) return FA_ERR_INVALID_ARG;
+        if ((int64_t)B * max_pages > (int64_t)INT32_MAX) return FA_ERR_TOO_LARGE;
+        // one page's rows of one head must stay inside a 32-bit buffer range
+        if ((uint64_t)page_size * H * D * 2 >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    }
     DecodePlan pl;
-    const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, &pl);
+    const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, paged, &pl);
     if (rc != FA_OK) return rc;
     if (pl.empty) return FA_OK;
     if (workspace_bytes < 0) return FA_ERR_INVALID_ARG;
 
     // ---- pointers ---------------------------------------------------------------
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+    if (paged && (!block_table || !seq_lens)) return FA_ERR_INVALID_ARG;
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return FA_ERR_INVALID_ARG;
     const uintptr_t pq = (uintptr_t)q, pk = (uintptr_t)k, pv = (uintptr_t)v, po = (uintptr_t)o,
                     pl_ = (uintptr_t)lse, pw = (uintptr_t)workspace;
     if ((pq | pk | pv | po) & 15u) return FA_ERR_ALIGNMENT;
     if (lse && (pl_ & 3u)) return FA_ERR_ALIGNMENT;
     if (pl.ws_bytes > 0 && (pw & 15u)) return FA_ERR_ALIGNMENT;
+    if (paged && (((uintptr_t)block_table | (uintptr_t)seq_lens) & 3u)) return FA_ERR_ALIGNMENT;
     const uint64_t bh = (uint64_t)B * H;
-    const uint64_t qbytes = bh * Sq * D * 2, kvbytes = bh * Sk * D * 2, lbytes = bh * Sq * 4;
+    const uint64_t qbytes = bh * Sq * D * 2, lbytes = bh * Sq * 4;
+    const uint64_t kvbytes = paged ? (uint64_t)num_pages * page_size * H * D * 2 : bh * Sk * D * 2;
     const uint64_t wbytes = (uint64_t)pl.ws_bytes;
     // outputs and workspace must not overlap the inputs or each other
     const uintptr_t outs[3] = {po, pl_, pw};
     const uint64_t outn[3] = {qbytes, lse ? lbytes : 0, wbytes};
-    const uintptr_t ins[3] = {pq, pk, pv};
-    const uint64_t inn[3] = {qbytes, kvbytes, kvbytes};
+    const uintptr_t ins[5] = {pq, pk, pv, (uintptr_t)block_table, (uintptr_t)seq_lens};
+    const uint64_t inn[5] = {qbytes, kvbytes, kvbytes, paged ? (uint64_t)B * max_pages * 4 : 0,
+                             paged ? (uint64_t)B * 4 : 0};
     for (int a = 0; a < 3; ++a) {
         if (!outn[a]) continue;
-        for (int b = 0; b < 3; ++b)
-            if (overlaps(outs[a], outn[a], ins[b], inn[b])) return FA_ERR_INVALID_ARG;
+        for (int b = 0; b < 5; ++b)
+            if (inn[b] && overlaps(outs[a], outn[a], ins[b], inn[b])) return FA_ERR_INVALID_ARG;
         for (int b = a + 1; b < 3; ++b)
             if (outn[b] && overlaps(outs[a], outn[a], outs[b], outn[b])) return FA_ERR_INVALID_ARG;
     }
@@ -303,16 +336,39 @@ extern "C" int fa_decode(const void *q, const void *k, const void *v, void *o, f
     p.H = H;
     p.Sq = Sq;
     p.Sk = Sk;
-    p.pos0 = Sk - Sq;
     p.win_lo = pl.win_lo;
     p.win_hi = pl.win_hi;
     p.c2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);  // as in fa_fwd
     p.negate_q = scale < 0.0f;
-    p.t_first = pl.t_first;
-    p.t_last = pl.t_last;
     p.tiles_per_split = pl.tiles_per_split;
     p.nsplit = pl.nsplit;
+    p.block_table = paged ? block_table : nullptr;
+    p.seq_lens = paged ? seq_lens : nullptr;
+    p.page_size = paged ? page_size : 0;
+    p.max_pages = paged ? max_pages : 0;
+    p.num_pages = paged ? num_pages : 0;
     hipError_t err = fa::launch_decode(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                         int B, int H, int Sq, int Sk, int D, float scale, int mask_mode,
+                         int win_l, int win_r, int dtype, void *workspace,
+                         int64_t workspace_bytes, hipStream_t stream) {
+    return decode_common(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
+                         workspace, workspace_bytes, stream, nullptr, nullptr, 0, 0, 0);
+}
+
+extern "C" int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
+                               float *lse, const int32_t *block_table, const int32_t *seq_lens,
+                               int B, int H, int Sq, int max_seq_len, int D, int num_pages,
+                               int page_size, int max_pages, float scale, int mask_mode,
+                               int win_l, int win_r, int dtype, void *workspace,
+                               int64_t workspace_bytes, hipStream_t stream) {
+    if (page_size == 0) return FA_ERR_UNSUPPORTED;  // 0 would mean "not paged" below
+    return decode_common(q, k_pages, v_pages, o, lse, B, H, Sq, max_seq_len, D, scale, mask_mode,
+                         win_l, win_r, dtype, workspace, workspace_bytes, stream, block_table,
+                         seq_lens, num_pages, page_size, max_pages);
+}

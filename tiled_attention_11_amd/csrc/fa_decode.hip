@@ -28,6 +28,14 @@
 //    kernel combines the splits of a row: LSE = log sum_s e^LSE_s and
 //    O = sum_s e^(LSE_s - LSE) O_s. With one split the wave writes O and LSE
 //    itself.
+//  * Paged cache: the keys of a sequence live in fixed-size pages of a pool
+//    [num_pages, page_size, H, D] named by a per-sequence block table, each
+//    sequence with its own length (both device arrays). A 32-key tile lies in
+//    one page, so only the tile's base address and row stride change; a page
+//    index outside the pool gets an empty buffer resource (its keys read as
+//    zero, nothing outside the pool is touched). Splits are laid over each
+//    sequence's own visible tiles; a split with none left reports no keys
+//    (LSE -inf), which the merge weighs zero.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -87,13 +95,23 @@ struct Decode {
         const int l32 = lane & 31, g = lane >> 5;
         const int ns = p.nsplit;
         const int bh = blockIdx.x / ns, sp = blockIdx.x - bh * ns;
-        const int ta = p.t_first + sp * p.tiles_per_split;
-        const int nt = min(ta + p.tiles_per_split, p.t_last + 1) - ta;  // >= 1
-        const int S = p.Sk, Sq = p.Sq;
-        const int64_t kv_head = (int64_t)bh * S * D;
-        const uint16_t *kh = static_cast<const uint16_t *>(p.k) + kv_head;
-        const uint16_t *vh = static_cast<const uint16_t *>(p.v) + kv_head;
+        const int bb = bh / p.H, hh = bh - bb * p.H;
+        const bool paged = p.block_table != nullptr;
+        // This sequence's cached keys and the tiles its rows can see (row i at
+        // position S - Sq + i); this split's share of them (possibly none).
+        const int S = paged ? min(max(__builtin_amdgcn_readfirstlane(p.seq_lens[bb]), 0), p.Sk)
+                            : p.Sk;
+        const int Sq = p.Sq;
+        const int win_lo = p.win_lo, win_hi = p.win_hi;
+        const int pos_first = S - Sq, pos_last = S - 1;
+        const int key_lo = max(0, pos_first - win_lo);
+        const int key_hi = min(S - 1, pos_last + win_hi);
+        const int ta = key_lo / BN + sp * p.tiles_per_split;
+        const int nt = key_hi < key_lo ? 0 : min(ta + p.tiles_per_split, key_hi / BN + 1) - ta;
         const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+        // Bytes between consecutive keys of one head: a contiguous [B, H, Sk, D]
+        // cache has them adjacent, a page pool interleaves the heads.
+        const uint32_t rs = paged ? (uint32_t)p.H * G::RB : (uint32_t)G::RB;
 
         // DMA: 1 KiB block b of a tile holds rows b * ROWS_PER_KB + lane / CPR;
         // lane L lands in physical chunk L % CPR and so fetches the logical
@@ -104,15 +122,26 @@ struct Decode {
 #pragma unroll
             for (int b = 0; b < G::NBLK; ++b) {
                 const int row = b * G::ROWS_PER_KB + lane / G::CPR;
-                kdma[b] = row * G::RB + kchunk<D>(pc, row) * 16;
-                vdma[b] = row * G::RB + vchunk<D>(pc, row) * 16;
+                kdma[b] = row * rs + kchunk<D>(pc, row) * 16;
+                vdma[b] = row * rs + vchunk<D>(pc, row) * 16;
             }
         }
         auto load = [&](int i) {  // tile ta + i into stage i % NSTAGE
             const int k0 = (ta + i) * BN;
-            const uint32_t bytes = (uint32_t)(S - k0) * G::RB;  // rows past S read as zero
-            const i32x4 rk = buffer_rsrc(kh + (int64_t)k0 * D, bytes);
-            const i32x4 rv = buffer_rsrc(vh + (int64_t)k0 * D, bytes);
+            const int rows = min(BN, S - k0);  // rows past S read as zero
+            int64_t first;  // element offset of (key k0, head hh) in k and v
+            bool ok = true;
+            if (paged) {
+                const int page = __builtin_amdgcn_readfirstlane(
+                    p.block_table[(int64_t)bb * p.max_pages + k0 / p.page_size]);
+                ok = page >= 0 && page < p.num_pages;
+                first = (((int64_t)page * p.page_size + k0 % p.page_size) * p.H + hh) * D;
+            } else {
+                first = ((int64_t)bh * p.Sk + k0) * D;
+            }
+            const uint32_t bytes = ok ? (uint32_t)(rows - 1) * rs + G::RB : 0u;
+            const i32x4 rk = buffer_rsrc(static_cast<const uint16_t *>(p.k) + (ok ? first : 0), bytes);
+            const i32x4 rv = buffer_rsrc(static_cast<const uint16_t *>(p.v) + (ok ? first : 0), bytes);
             const uint32_t base = smem_addr + (uint32_t)((i % G::NSTAGE) * G::STAGE_BYTES);
 #pragma unroll
             for (int b = 0; b < G::NBLK; ++b) dma16(rk, base + (uint32_t)b * 1024u, kdma[b]);
@@ -165,9 +194,7 @@ struct Decode {
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
         float m_run = -INFINITY, l_run = 0.0f;
         const float c2 = p.c2;
-        const int pos = p.pos0 + l32;  // this lane's query position
-        const int pos_first = p.pos0, pos_last = p.pos0 + Sq - 1;
-        const int win_lo = p.win_lo, win_hi = p.win_hi;
+        const int pos = pos_first + l32;  // this lane's query position
 
         for (int i = 0; i < nt; ++i) {
             if (i + G::NSTAGE - 1 < nt) load(i + G::NSTAGE - 1);  // into the stage tile i - 1 used

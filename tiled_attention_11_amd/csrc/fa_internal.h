@@ -48,19 +48,27 @@ constexpr int kDecodeMaxRows = 32;
 
 struct DecodeParams {
     const void *q;          // [B, H, Sq, D]
-    const void *k, *v;      // [B, H, Sk, D]
+    const void *k, *v;      // [B, H, Sk, D], or page pools (below)
     void *o;                // [B, H, Sq, D]
     float *lse;             // [B, H, Sq] or nullptr
     float *ws_o;            // nsplit > 1: partial outputs [B*H, nsplit, Sq, D]
     float *ws_lse;          // nsplit > 1: partial LSEs [B*H, nsplit, Sq]
-    int B, H, Sq, Sk;
-    int pos0;               // Sk - Sq: position of query row 0 in the sequence
+    int B, H, Sq;
+    int Sk;                 // cached keys per sequence (paged: the largest seq_lens allows)
     int win_lo, win_hi;     // as in FwdParams, relative to each row's position
     float c2;
     int negate_q;
-    int t_first, t_last;    // key tiles visible from some row (same for every head)
-    int tiles_per_split;    // a split covers this many consecutive tiles (the last may have fewer)
+    // Splits: split s of a head covers tiles t0 + s*tiles_per_split .. +tiles_per_split-1,
+    // clipped to the tiles visible from its sequence's rows; t0 is the first such tile.
+    int tiles_per_split;
     int nsplit;             // splits per head; 1 writes o and lse directly
+    // Paged cache (block_table != nullptr): k and v are pools [num_pages, page_size,
+    // H, D]; key j of sequence b is row j % page_size of page
+    // block_table[b * max_pages + j / page_size] (page_size a multiple of the tile),
+    // and sequence b caches min(seq_lens[b], Sk) keys.
+    const int32_t *block_table;
+    const int32_t *seq_lens;
+    int page_size, max_pages, num_pages;
 };
 
 // Enqueue the cache kernel (and, for nsplit > 1, the merge kernel).
