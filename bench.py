@@ -143,14 +143,27 @@ def bench_decode(args, name):
     tq, tk, tv = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
     out = torch.empty_like(tq)
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
-    need = fa.fa_decode_workspace_bytes(B, H, Sq, Sk, D, m, wl, wr)
+    ps = w.get("page_size")
+    if ps:
+        kp, vp, table = synth.paged_cache(k, v, ps, w["seed"])
+        tkp, tvp = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (kp, vp))
+        ttab = torch.from_numpy(table).to(dev)
+        tlen = torch.full((B,), Sk, dtype=torch.int32, device=dev)
+        del tk, tv
+        need = fa.fa_decode_paged_workspace_bytes(B, H, Sq, Sk, D, m, wl, wr)
+    else:
+        need = fa.fa_decode_workspace_bytes(B, H, Sq, Sk, D, m, wl, wr)
     ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
     print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s, workspace "
           f"{need} B", file=sys.stderr, flush=True)
 
     def step():
-        fa.decode(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
-                  lse=lse, workspace=ws)
+        if ps:
+            fa.decode_paged(tq, tkp, tvp, ttab, tlen, Sk, scale=w["scale"], mask=w["mask"],
+                            window=(wl, wr), out=out, lse=lse, workspace=ws)
+        else:
+            fa.decode(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
+                      lse=lse, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -190,7 +203,8 @@ def bench_decode(args, name):
         "data": "synthetic",
         "config": {
             "workload": (f"{name}: B={B} H={H} Sq={Sq} Sk={Sk} D={D} {dtype} {w['mask']}"
-                         f" scale={w['scale']:.6g}"),
+                         + (f" paged {ps}-key pages, shuffled" if ps else "")
+                         + f" scale={w['scale']:.6g}"),
             "B": B, "H": H, "Sq": Sq, "Sk": Sk, "D": D, "mask": w["mask"], "window": [wl, wr],
             "bytes_per_step": nbytes, "flops_per_step": flops, "workspace_bytes": int(need),
         },

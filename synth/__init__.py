@@ -57,7 +57,28 @@ DECODE_WORKLOADS = {
                                     mask="causal", window=(-1, -1), scale=128 ** -0.5, seed=7),
     "decode_b4h32_q16_k16384": dict(B=4, H=32, Sq=16, Sk=16384, D=128, dtype="f16",
                                     mask="causal", window=(-1, -1), scale=128 ** -0.5, seed=8),
+    # the same cache scattered over 64-key pages of a pool in a seeded random order
+    "decode_paged_b4h32_q1_k16384": dict(B=4, H=32, Sq=1, Sk=16384, D=128, dtype="f16",
+                                         mask="causal", window=(-1, -1), scale=128 ** -0.5,
+                                         seed=7, page_size=64),
 }
+
+
+def paged_cache(k, v, page_size, seed):
+    """Scatter contiguous caches k, v [B, H, Sk, D] (Sk a multiple of page_size)
+    over the pages of pools [B * Sk / page_size, page_size, H, D] in a seeded
+    random order; return the pools and the int32 block table [B, Sk / page_size]."""
+    B, H, Sk, D = k.shape
+    per = Sk // page_size
+    order = np.random.default_rng(seed).permutation(B * per).astype(np.int32)
+    table = order.reshape(B, per)
+    kp = np.empty((B * per, page_size, H, D), dtype=k.dtype)
+    vp = np.empty_like(kp)
+    src_k = k.reshape(B, H, per, page_size, D).transpose(0, 2, 3, 1, 4).reshape(B * per, page_size, H, D)
+    src_v = v.reshape(B, H, per, page_size, D).transpose(0, 2, 3, 1, 4).reshape(B * per, page_size, H, D)
+    kp[table.reshape(-1)] = src_k
+    vp[table.reshape(-1)] = src_v
+    return kp, vp, table
 
 
 def f32_to_bits(x, dtype):
