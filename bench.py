@@ -8,7 +8,9 @@ and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
 With ``--workload decode_*`` one step is one fa_decode call (new query rows
 against a key/value cache, HBM-bound): the line reports GB/s of algorithmic
-bytes against the 8 TB/s HBM peak instead.
+bytes against the 8 TB/s HBM peak instead. With ``--workload varlen_*`` one
+step is one fa_fwd_varlen call over a packed batch of ragged sequences
+(TFLOP/s over the visible pairs of every sequence).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds T]
 """
@@ -253,6 +255,130 @@ def bench_decode(args, name):
     print(json.dumps(result), flush=True)
 
 
+def bench_varlen(args, name):
+    import numpy as np
+    import torch
+
+    import synth
+    import tiled_attention_11_amd as fa
+
+    w = synth.VARLEN_WORKLOADS[name]
+    T, H, D, dtype = w["T"], w["H"], w["D"], w["dtype"]
+    wl, wr = w["window"]
+    m = fa._mask_code(w["mask"])
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v, cu = synth.varlen_inputs(name)
+    lengths = np.diff(cu)
+    max_seqlen = int(lengths.max())
+    tq, tk, tv = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
+    tcu = torch.from_numpy(cu).to(dev)
+    out = torch.empty_like(tq)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s, lengths "
+          f"{lengths.tolist()}", file=sys.stderr, flush=True)
+
+    def step():
+        fa.forward_varlen(tq, tk, tv, tcu, max_seqlen, scale=w["scale"], mask=w["mask"],
+                          window=(wl, wr), out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]) * 1e-3
+    avg_s = evs[0].elapsed_time(evs[-1]) * 1e-3 / args.steps
+    print(f"[bench] timed {args.steps} steps: avg {avg_s * 1e6:.1f} us, median "
+          f"{np.median(per) * 1e6:.1f} us", file=sys.stderr, flush=True)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+
+    flops = fa.fa_fwd_varlen_flops(cu.tolist(), H, D, m, wl, wr)
+    tflops = flops / avg_s / 1e12
+    result = {
+        "metric": "packed variable-length attention fwd TFLOP/s and % of fp16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(avg_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{name}: {len(lengths)} sequences packed into T={T} tokens, "
+                         f"lengths uniform in [{w['len_lo']}, {w['len_hi']}] (seed {w['seed']}), "
+                         f"H={H} D={D} {dtype} {w['mask']} scale={w['scale']:.6g}"),
+            "T": T, "H": H, "D": D, "lengths": lengths.tolist(), "mask": w["mask"],
+            "window": [wl, wr], "flops_per_step": flops,
+        },
+        "pct_of_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 2),
+        "median_launch_us": round(float(np.median(per)) * 1e6, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+            "traffic": counted_traffic(name),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        from tests.parity import compare
+        orc = oracle.load()
+        o_bits = out.cpu().view(torch.int16).numpy().view(np.uint16)
+        lse_h = lse.cpu().numpy()
+        # query rows drawn uniformly from each sequence in turn, until the
+        # time budget is spent
+        rng = np.random.default_rng(1234)
+        t_used, pairs, nrows, stats, rounds = 0.0, 0, 0, [], 0
+        while t_used < args.cpu_seconds and rounds < 64:
+            rounds += 1
+            for a, b in zip(cu[:-1], cu[1:]):
+                L = int(b - a)
+                rows_i = rng.integers(0, L, 4)
+                heads = rng.integers(0, H, 4)
+
+                def head_major(x):
+                    return np.ascontiguousarray(x[a:b].transpose(1, 0, 2))[None]
+
+                hq, hk, hv = head_major(q), head_major(k), head_major(v)
+                t1 = time.perf_counter()
+                o_ref, lse_ref = orc.attention_rows(hq, hk, hv, dtype, w["scale"], w["mask"],
+                                                    (wl, wr), rows=heads * L + rows_i)
+                t_used += time.perf_counter() - t1
+                stats.append(compare(o_bits[a + rows_i, heads], lse_h[a + rows_i, heads],
+                                     o_ref, lse_ref, dtype))
+                pairs += int(visible_per_row(L, w["mask"], (wl, wr), rows_i).sum())
+                nrows += rows_i.size
+        result["cpu_baseline"] = {
+            "value": round(4 * D * pairs / t_used / 1e12, 6), "unit": "TFLOP/s",
+            "cores": orc.max_threads(), "kind": "oracle",
+            "sample": (f"{nrows} query rows, 4 per sequence per round over {rounds} rounds "
+                       f"(seed 1234), {pairs} visible pairs, {t_used:.2f} s wall, fp64"),
+        }
+        result["parity_sample"] = {"rows": nrows, "pass": all(s["pass"] for s in stats),
+                                   "max_abs": max(s["max_abs"] for s in stats),
+                                   "lse_max_abs": max(s.get("lse_max_abs", 0.0) for s in stats)}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +408,8 @@ def main():
     name = args.workload or synth.HEADLINE
     if name in synth.DECODE_WORKLOADS:
         return bench_decode(args, name)
+    if name in synth.VARLEN_WORKLOADS:
+        return bench_varlen(args, name)
     w = synth.WORKLOADS[name]
     B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
     wl, wr = w["window"]

@@ -61,7 +61,8 @@ typedef enum {
     FA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum, non-finite
                                 scale, output overlapping an input */
     FA_ERR_UNSUPPORTED = -2, /* head dimension other than 64 or 128 */
-    FA_ERR_ALIGNMENT = -3,   /* q/k/v/o not 16-byte aligned, lse not 4-byte aligned */
+    FA_ERR_ALIGNMENT = -3,   /* q/k/v/o not 16-byte aligned, lse or an index array
+                                not 4-byte aligned */
     FA_ERR_TOO_LARGE = -4,   /* a head's [S, D] block is 2^31 bytes or more, or the
                                 launch grid or FLOP count would overflow */
     FA_ERR_HIP = -5          /* the HIP runtime rejected the kernel launch */
@@ -114,6 +115,54 @@ int64_t fa_visible_pairs(int S, int mask_mode, int win_l, int win_r);
  * negative fa_status.
  */
 int64_t fa_fwd_flops(int B, int H, int S, int D, int mask_mode, int win_l, int win_r);
+
+/*
+ * fa_fwd_varlen -- fa_fwd over a batch of sequences of different lengths
+ * packed token after token: sequence b holds tokens cu_seqlens[b] ..
+ * cu_seqlens[b+1] - 1 of the packed tensors and attends only within itself,
+ * its token cu_seqlens[b] + i being its query/key row i (the mask applies to
+ * those row numbers). Defining passage: Ascend C FlashAttention-2 tile-fusion
+ * page (ascendai.csdn.net), section 4.1 (data structures), which takes the
+ * input as contiguous [total_tokens, H, D]; the per-sequence attention is
+ * fa_fwd's.
+ *
+ * q, k, v      device pointers, contiguous [total_tokens, H, D] of `dtype`
+ *              (D fastest, then heads, then tokens); read only.
+ * o            device pointer, [total_tokens, H, D] of `dtype`; every token
+ *              that lies in a sequence is overwritten (RNE), others are not
+ *              touched.
+ * lse          device pointer to fp32 [total_tokens, H], or NULL; written like o.
+ * cu_seqlens   device pointer, int32 [nseq + 1], non-decreasing, cu_seqlens[0]
+ *              normally 0 and cu_seqlens[nseq] <= total_tokens; read only. The
+ *              kernel clamps each offset into [0, total_tokens] (and each end to
+ *              at least its start) and attends over at most max_seqlen tokens of
+ *              a sequence, so no bad value makes it touch memory outside the
+ *              tensors; rows of overlapping sequences get unspecified values.
+ * nseq         number of sequences (>= 0).
+ * max_seqlen   host-side bound on every sequence's length (>= 0); tokens past it
+ *              are not written. If nseq*H*max_seqlen == 0 or total_tokens == 0
+ *              the call does nothing and returns FA_OK.
+ * total_tokens rows of the packed tensors (>= 0).
+ * H, D, scale, mask_mode, win_l, win_r, dtype, stream: as for fa_fwd.
+ *
+ * Limits: max_seqlen * H * D * 2 < 2^31 (FA_ERR_TOO_LARGE otherwise).
+ * cu_seqlens needs 4-byte alignment and must not overlap o or lse.
+ * Ownership and arithmetic as fa_fwd; each sequence's result is bitwise the
+ * one fa_fwd gives for that sequence alone in [1, H, L, D] layout.
+ */
+int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                  const int32_t *cu_seqlens, int nseq, int max_seqlen, int total_tokens,
+                  int H, int D, float scale, int mask_mode, int win_l, int win_r,
+                  int dtype, hipStream_t stream);
+
+/*
+ * fa_fwd_varlen_flops -- the algorithmic FLOPs of one fa_fwd_varlen call:
+ * the sum over sequences of 4 * D * H * fa_visible_pairs(length). cu_seqlens is
+ * a HOST pointer to int32 [nseq + 1] (non-negative, non-decreasing; otherwise
+ * FA_ERR_INVALID_ARG). Returns the count, or a negative fa_status.
+ */
+int64_t fa_fwd_varlen_flops(const int32_t *cu_seqlens, int nseq, int H, int D,
+                            int mask_mode, int win_l, int win_r);
 
 /*
  * fa_decode -- attention of Sq new query rows against a key/value cache

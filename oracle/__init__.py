@@ -159,6 +159,42 @@ class Oracle:
             raise ValueError("oracle_attention_kv rejected its arguments")
         return o, lse
 
+    def attention_varlen(self, q, k, v, cu_seqlens, dtype, scale, mask, window=(-1, -1),
+                         nthreads=0):
+        """Packed variable-length sequences, each attending only within itself.
+
+        Ascend C FlashAttention-2 tile-fusion page, section 4.1 (data
+        structures): the input is taken as contiguous [total_tokens, H, D].
+        Sequence b is tokens ``cu_seqlens[b] .. cu_seqlens[b+1]-1`` (host ints,
+        non-decreasing, within the tensors); its token ``cu_seqlens[b] + i`` is
+        its row i, and its result is :meth:`attention` of that sequence alone.
+        Returns ``(o [T,H,D] float64, lse [T,H] float64)``; tokens in no
+        sequence are NaN.
+        """
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+        if q.ndim != 3 or q.shape != k.shape or q.shape != v.shape:
+            raise ValueError("q, k, v must share one [total_tokens, H, D] shape")
+        T, H, D = q.shape
+        cu = [int(x) for x in cu_seqlens]
+        if any(b < a for a, b in zip(cu, cu[1:])) or (cu and (cu[0] < 0 or cu[-1] > T)):
+            raise ValueError("cu_seqlens must be non-decreasing within [0, total_tokens]")
+        o = np.full((T, H, D), np.nan)
+        lse = np.full((T, H), np.nan)
+        for a, b in zip(cu, cu[1:]):
+            if b == a:
+                continue
+
+            def head_major(x):  # [L, H, D] -> [1, H, L, D]
+                return np.ascontiguousarray(x[a:b].transpose(1, 0, 2))[None]
+
+            os_, ls = self.attention(head_major(q), head_major(k), head_major(v), dtype,
+                                     scale, mask, window, nthreads)
+            o[a:b] = os_[0].transpose(1, 0, 2)
+            lse[a:b] = ls[0].T
+        return o, lse
+
     def max_threads(self):
         return int(self.lib.oracle_max_threads())
 

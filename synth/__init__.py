@@ -45,6 +45,17 @@ WORKLOADS = {
 
 HEADLINE = "b4h32s4096_causal"
 
+# Packed variable-length batches ([total_tokens, H, D], one token after the
+# other; the tile-fusion page's data-structure section takes this layout).
+# The lengths are drawn uniformly from [len_lo, len_hi] (varlen_lengths), so
+# most are not multiples of a tile: the same 16384 tokens as the headline
+# B4 x S4096 batch, in about eight sequences of ragged lengths.
+VARLEN_WORKLOADS = {
+    "varlen_h32_t16384_causal": dict(T=16384, H=32, D=128, dtype="f16", mask="causal",
+                                     window=(-1, -1), scale=128 ** -0.5, seed=9,
+                                     len_lo=256, len_hi=4096),
+}
+
 # New query rows against a key/value cache (incremental decoding): Sq rows at
 # the end of sequences whose first Sk positions the cache holds. The NPU
 # optimisation page's hands-on section runs batch 1, 32 heads, D = 128 against
@@ -109,6 +120,44 @@ def make_qkv(B, H, S, D, dtype, seed, outlier_frac=0.0, outlier_scale=20.0):
                     rows = rng.choice(S, size=n, replace=False)
                     k[b, h, rows, :] *= np.float32(outlier_scale)
     return f32_to_bits(q, dtype), f32_to_bits(k, dtype), f32_to_bits(v, dtype)
+
+
+def varlen_lengths(total_tokens, len_lo, len_hi, seed):
+    """Sequence lengths for a packed batch of ``total_tokens`` tokens: integers
+    drawn uniformly from [len_lo, len_hi] with ``default_rng(seed)`` until they
+    reach the total, the last one cut so that they sum to it exactly."""
+    rng = np.random.default_rng(seed)
+    lengths, left = [], int(total_tokens)
+    while left > 0:
+        n = min(int(rng.integers(len_lo, len_hi + 1)), left)
+        lengths.append(n)
+        left -= n
+    return lengths
+
+
+def cu_seqlens_of(lengths):
+    """int32 [nseq + 1] prefix sums of ``lengths`` (starting at 0)."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))]).astype(np.int32)
+
+
+def make_varlen_qkv(total_tokens, H, D, dtype, seed):
+    """Packed q, k, v of ``total_tokens`` tokens: standard normal fp32 drawn in
+    the order q, k, v, each [total_tokens, H, D] in C order from one generator,
+    each rounded once to ``dtype`` (uint16 bit patterns)."""
+    rng = np.random.default_rng(seed)
+    shape = (total_tokens, H, D)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    return f32_to_bits(q, dtype), f32_to_bits(k, dtype), f32_to_bits(v, dtype)
+
+
+def varlen_inputs(name):
+    """(q, k, v, cu_seqlens) for a named packed workload."""
+    w = VARLEN_WORKLOADS[name]
+    lengths = varlen_lengths(w["T"], w["len_lo"], w["len_hi"], w["seed"])
+    q, k, v = make_varlen_qkv(w["T"], w["H"], w["D"], w["dtype"], w["seed"] + 1)
+    return q, k, v, cu_seqlens_of(lengths)
 
 
 def make_decode_qkv(B, H, Sq, Sk, D, dtype, seed):

@@ -369,6 +369,43 @@ def pin_kv_sdpa(orc):
                 assert np.max(np.abs(lse - lse_ref)) < 1e-12, (dtype, Sq, Sk, mask, window)
 
 
+def pin_varlen_block_diagonal_sdpa(orc):
+    """Packed sequences match torch's CPU fp64 scaled_dot_product_attention
+    over the whole packed batch, per head, with a block-diagonal boolean mask
+    (the mask rule applied to each block's own row numbers), and
+    torch.logsumexp; tokens in no sequence stay NaN."""
+    from synth import cu_seqlens_of, make_varlen_qkv
+    for dtype in ("f16", "bf16"):
+        for lengths, extra in (([5, 1, 9, 0, 12], 0), ([17], 3), ([3, 3, 3, 3], 2)):
+            cu = cu_seqlens_of(lengths)
+            T = int(cu[-1]) + extra
+            q, k, v = make_varlen_qkv(T, 2, 8, dtype, seed=40 + T)
+            seq = np.full(T, -1)
+            row = np.zeros(T, dtype=np.int64)
+            for b, (a, e) in enumerate(zip(cu[:-1], cu[1:])):
+                seq[a:e] = b
+                row[a:e] = np.arange(e - a)
+            qd, kd, vd = (torch.from_numpy(_decode_ref(x, dtype)).transpose(0, 1) for x in (q, k, v))
+            for mask, window in MASK_CASES:
+                same = (seq[:, None] == seq[None, :]) & (seq[:, None] >= 0)
+                bm = same & _bool_mask_kv(T, T, mask, window)  # row i vs key j, positions
+                # _bool_mask_kv at Sq == Sk compares token indices; within one
+                # block those differ from the row numbers by the same offset.
+                if not bm[seq >= 0].any(axis=1).all():
+                    continue  # a row with no visible key: covered by the definition only
+                bmt = torch.from_numpy(bm)
+                keep = torch.from_numpy(seq >= 0)
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qd[:, keep], kd, vd, attn_mask=bmt[keep], scale=0.4).numpy()
+                scores = torch.matmul(qd, kd.transpose(-1, -2)) * 0.4
+                lse_ref = torch.logsumexp(scores.masked_fill(~bmt, float("-inf")), dim=-1)
+                o, lse = orc.attention_varlen(q, k, v, cu, dtype, 0.4, mask, window)
+                got = np.ascontiguousarray(o[seq >= 0].transpose(1, 0, 2))
+                assert np.max(np.abs(got - ref)) < 1e-12, (dtype, lengths, mask, window)
+                assert np.max(np.abs(lse[seq >= 0] - lse_ref.numpy().T[seq >= 0])) < 1e-12
+                assert np.isnan(o[seq < 0]).all() and np.isnan(lse[seq < 0]).all()
+
+
 def pin_kv_is_the_tail_of_the_square_case(orc):
     """New rows at the end of a sequence give the last rows of the square
     problem whose query rows end with them (any earlier query rows)."""
@@ -418,4 +455,5 @@ ALL_PINS = [
     pin_kv_sdpa,
     pin_kv_is_the_tail_of_the_square_case,
     pin_kv_uniform_weights,
+    pin_varlen_block_diagonal_sdpa,
 ]

@@ -1,12 +1,13 @@
 """Fused attention forward for AMD Instinct MI355X (gfx950).
 
 A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
-``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops``, ``fa_decode``,
-``fa_decode_workspace_bytes``, ``fa_decode_flops``, ``fa_decode_paged``,
-``fa_decode_paged_workspace_bytes`` and ``fa_strerror`` carry the C names and
-arguments (marshalling only). ``forward``, ``decode`` and ``decode_paged`` are
-the convenience entries for torch tensors: torch supplies device memory and
-the stream; every step of the computation runs in the library's HIP kernels.
+``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops``, ``fa_fwd_varlen``,
+``fa_fwd_varlen_flops``, ``fa_decode``, ``fa_decode_workspace_bytes``,
+``fa_decode_flops``, ``fa_decode_paged``, ``fa_decode_paged_workspace_bytes`` and
+``fa_strerror`` carry the C names and arguments (marshalling only).
+``forward``, ``forward_varlen``, ``decode`` and ``decode_paged`` are the
+convenience entries for torch tensors: torch supplies device memory and the
+stream; every step of the computation runs in the library's HIP kernels.
 There is no fallback: if the library is missing, importing this package
 raises.
 """
@@ -17,8 +18,9 @@ import os
 __all__ = [
     "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
     "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
-    "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
-    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "decode", "decode_paged",
+    "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
+    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "forward_varlen", "decode",
+    "decode_paged",
     "lib_path", "library",
 ]
 
@@ -56,6 +58,11 @@ def _load():
     lib.fa_fwd_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     lib.fa_fwd_flops.restype = ctypes.c_int64
     i64 = ctypes.c_int64
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float,
+                                  ci, ci, ci, ci, vp]
+    lib.fa_fwd_varlen.restype = ci
+    lib.fa_fwd_varlen_flops.argtypes = [ctypes.POINTER(ctypes.c_int32), ci, ci, ci, ci, ci, ci]
+    lib.fa_fwd_varlen_flops.restype = i64
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci,
                               ci, ci, vp, i64, vp]
     lib.fa_decode.restype = ci
@@ -101,6 +108,22 @@ def fa_visible_pairs(S, mask_mode, win_l=-1, win_r=-1):
 
 def fa_fwd_flops(B, H, S, D, mask_mode, win_l=-1, win_r=-1):
     return _lib.fa_fwd_flops(B, H, S, D, mask_mode, win_l, win_r)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, total_tokens, H, D, scale,
+                  mask_mode, win_l, win_r, dtype, stream):
+    """Call ``fa_fwd_varlen`` with raw device addresses (ints); return its status."""
+    return _lib.fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, total_tokens, H, D,
+                              scale, mask_mode, win_l, win_r, dtype, stream)
+
+
+def fa_fwd_varlen_flops(cu_seqlens, H, D, mask_mode, win_l=-1, win_r=-1):
+    """``cu_seqlens``: a host sequence of nseq + 1 ints."""
+    n = len(cu_seqlens) - 1
+    if n < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    arr = (ctypes.c_int32 * (n + 1))(*[int(x) for x in cu_seqlens])
+    return _lib.fa_fwd_varlen_flops(arr, n, H, D, mask_mode, win_l, win_r)
 
 
 def fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
@@ -191,6 +214,57 @@ def forward(q, k, v, *, scale=None, mask="full", window=(-1, -1), out=None, lse=
                         float(scale), _mask_code(mask), int(wl), int(wr), dtype, stream)
     if status != 0:
         raise FaError(status)
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen, *, scale=None, mask="full",
+                   window=(-1, -1), out=None, lse=None, return_lse=True, stream=None):
+    """Attention forward over packed variable-length sequences.
+
+    q, k, v: contiguous [total_tokens, H, D] float16 or bfloat16 tensors on one
+    GPU; sequence b is tokens ``cu_seqlens[b] .. cu_seqlens[b+1]-1``
+    (``cu_seqlens``: int32 device tensor [nseq + 1]); ``max_seqlen``: a host int
+    bounding every length. Other arguments as for ``forward``. Returns
+    ``(o, lse)`` with ``lse`` of shape [total_tokens, H].
+    """
+    import torch
+
+    if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [total_tokens, H, D] shape")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if (cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1 or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous()):
+        raise ValueError("cu_seqlens must be a contiguous int32 [nseq + 1] tensor on q's device")
+    T, H, D = q.shape
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (T, H) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [total_tokens, H] tensor on q's device")
+    wl, wr = window
+    dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        status = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr() if lse is not None else None,
+                               cu_seqlens.data_ptr(), nseq, int(max_seqlen), T, H, D,
+                               float(scale), _mask_code(mask), int(wl), int(wr), dtype, stream)
+    if status != 0:
+        raise FaError(status, "fa_fwd_varlen")
     return out, lse
 
 

@@ -48,6 +48,44 @@ bool overlaps(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) {
     return a < b + nb && b < a + na;
 }
 
+// Scores go to base 2 in one multiply by c2 = |scale| * log2(e). c2 is
+// floored at 2^-100: below that every visible score under 2^76 in magnitude
+// (any fp16 input gives |q.k| < 2^40) maps to under 2^-24, so exp2 of it is
+// exactly 1.0f, the same fp32 result as a zero scale, while c2 stays positive
+// and hidden scores (-inf) keep probability exactly 0.
+float base2_scale(float scale) {
+    return std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);
+}
+
+// Work distribution and launch of the forward kernel, for p with everything
+// but the fields set here filled in: one workgroup per CU (each takes a whole
+// CU), each running its share of the bh * n_qtiles query tiles; see FwdParams.
+int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t n_qtiles, int D, int dtype,
+                        hipStream_t stream) {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu <= 0)
+        return FA_ERR_HIP;
+    p.n_qtiles = (int)n_qtiles;
+    const uint64_t n_items = bh * n_qtiles;
+    uint64_t grid = n_items < (uint64_t)n_cu ? n_items : (uint64_t)n_cu;
+    const bool xcd = bh % kNumXcd == 0 && grid >= (uint64_t)kNumXcd;
+    if (xcd) grid -= grid % kNumXcd;
+    const uint64_t list_heads = xcd ? bh / kNumXcd : bh;
+    const uint64_t nj = xcd ? grid / kNumXcd : grid;  // workgroups per list
+    // Heads per group: enough that a round of nj positions covers about one
+    // group, so the workgroups of a list share few heads at a time.
+    uint64_t gh = 1;
+    while (2 * gh * n_qtiles <= nj && list_heads % (2 * gh) == 0) gh *= 2;
+    p.grid = (int)grid;
+    p.xcd_lists = xcd;
+    p.list_len = (int)(list_heads * n_qtiles);
+    p.group_heads = (int)gh;
+    hipError_t err = fa::launch_fwd(p, D, dtype, stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" int64_t fa_visible_pairs(int S, int mask_mode, int win_l, int win_r) {
@@ -79,7 +117,8 @@ extern "C" const char *fa_strerror(int status) {
     case FA_OK: return "success";
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128 only)";
-    case FA_ERR_ALIGNMENT: return "misaligned pointer (q/k/v/o need 16 bytes, lse 4)";
+    case FA_ERR_ALIGNMENT:
+        return "misaligned pointer (q/k/v/o need 16 bytes, lse and index arrays 4)";
     case FA_ERR_TOO_LARGE: return "problem too large for the kernel's index ranges";
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
     default: return "unknown status";
@@ -132,40 +171,90 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
     p.B = B;
     p.H = H;
     p.S = S;
-    p.n_qtiles = (int)n_qtiles;
     p.win_lo = win_lo;
     p.win_hi = win_hi;
-    // Scores go to base 2 in one multiply by c2 = |scale| * log2(e). c2 is
-    // floored at 2^-100: below that every visible score under 2^76 in
-    // magnitude (any fp16 input gives |q.k| < 2^40) maps to under 2^-24, so
-    // exp2 of it is exactly 1.0f, the same fp32 result as a zero scale, while
-    // c2 stays positive and hidden scores (-inf) keep probability exactly 0.
-    p.c2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);
+    p.c2 = base2_scale(scale);
     p.negate_q = scale < 0.0f;
+    p.row_stride = D;
+    p.cu_seqlens = nullptr;
+    p.total_tokens = 0;
+    return plan_and_launch_fwd(p, bh, n_qtiles, D, dtype, stream);
+}
 
-    // One workgroup per CU (each takes a whole CU), each running its share of
-    // the bh * n_qtiles query tiles; see FwdParams.
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n_cu <= 0)
-        return FA_ERR_HIP;
-    const uint64_t n_items = bh * n_qtiles;
-    uint64_t grid = n_items < (uint64_t)n_cu ? n_items : (uint64_t)n_cu;
-    const bool xcd = bh % kNumXcd == 0 && grid >= (uint64_t)kNumXcd;
-    if (xcd) grid -= grid % kNumXcd;
-    const uint64_t list_heads = xcd ? bh / kNumXcd : bh;
-    const uint64_t nj = xcd ? grid / kNumXcd : grid;  // workgroups per list
-    // Heads per group: enough that a round of nj positions covers about one
-    // group, so the workgroups of a list share few heads at a time.
-    uint64_t gh = 1;
-    while (2 * gh * n_qtiles <= nj && list_heads % (2 * gh) == 0) gh *= 2;
-    p.grid = (int)grid;
-    p.xcd_lists = xcd;
-    p.list_len = (int)(list_heads * n_qtiles);
-    p.group_heads = (int)gh;
-    hipError_t err = fa::launch_fwd(p, D, dtype, stream);
-    return err == hipSuccess ? FA_OK : FA_ERR_HIP;
+extern "C" int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                             const int32_t *cu_seqlens, int nseq, int max_seqlen,
+                             int total_tokens, int H, int D, float scale, int mask_mode,
+                             int win_l, int win_r, int dtype, hipStream_t stream) {
+    // ---- scalar arguments -------------------------------------------------
+    if (nseq < 0 || max_seqlen < 0 || total_tokens < 0 || H < 0) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    int win_lo, win_hi;
+    if (!window_of(mask_mode, win_l, win_r, &win_lo, &win_hi)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)nseq * H * max_seqlen == 0 || total_tokens == 0) return FA_OK;
+
+    // ---- sizes ------------------------------------------------------------
+    // One head of one sequence spans (max_seqlen - 1) token rows of H * D
+    // elements plus one row: the kernel's 32-bit buffer ranges must hold it.
+    const uint64_t row_bytes = (uint64_t)H * D * 2;
+    if ((uint64_t)max_seqlen * row_bytes >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    const uint64_t bh = (uint64_t)nseq * H;
+    const uint64_t n_qtiles = ((uint64_t)max_seqlen + fa::kBlockM - 1) / fa::kBlockM;
+    if (bh * n_qtiles > (uint64_t)INT32_MAX) return FA_ERR_TOO_LARGE;
+    const __int128 tensor_bytes = (__int128)total_tokens * row_bytes;
+    if (tensor_bytes > (__int128)INT64_MAX / 4) return FA_ERR_TOO_LARGE;
+
+    // ---- pointers ---------------------------------------------------------
+    if (!q || !k || !v || !o || !cu_seqlens) return FA_ERR_INVALID_ARG;
+    const uintptr_t pq = (uintptr_t)q, pk = (uintptr_t)k, pv = (uintptr_t)v,
+                    po = (uintptr_t)o, pl = (uintptr_t)lse, pc = (uintptr_t)cu_seqlens;
+    if ((pq | pk | pv | po) & 15u) return FA_ERR_ALIGNMENT;
+    if ((lse && (pl & 3u)) || (pc & 3u)) return FA_ERR_ALIGNMENT;
+    const uint64_t nbytes = (uint64_t)tensor_bytes;
+    const uint64_t lbytes = (uint64_t)total_tokens * H * 4;
+    const uint64_t cbytes = ((uint64_t)nseq + 1) * 4;
+    if (overlaps(po, nbytes, pq, nbytes) || overlaps(po, nbytes, pk, nbytes) ||
+        overlaps(po, nbytes, pv, nbytes) || overlaps(po, nbytes, pc, cbytes))
+        return FA_ERR_INVALID_ARG;
+    if (lse && (overlaps(pl, lbytes, pq, nbytes) || overlaps(pl, lbytes, pk, nbytes) ||
+                overlaps(pl, lbytes, pv, nbytes) || overlaps(pl, lbytes, po, nbytes) ||
+                overlaps(pl, lbytes, pc, cbytes)))
+        return FA_ERR_INVALID_ARG;
+
+    // ---- launch -----------------------------------------------------------
+    fa::FwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.B = nseq;
+    p.H = H;
+    p.S = max_seqlen;
+    p.win_lo = win_lo;
+    p.win_hi = win_hi;
+    p.c2 = base2_scale(scale);
+    p.negate_q = scale < 0.0f;
+    p.row_stride = H * D;
+    p.cu_seqlens = cu_seqlens;
+    p.total_tokens = total_tokens;
+    return plan_and_launch_fwd(p, bh, n_qtiles, D, dtype, stream);
+}
+
+extern "C" int64_t fa_fwd_varlen_flops(const int32_t *cu_seqlens, int nseq, int H, int D,
+                                       int mask_mode, int win_l, int win_r) {
+    if (nseq < 0 || H < 0 || D <= 0 || (nseq > 0 && !cu_seqlens)) return FA_ERR_INVALID_ARG;
+    __int128 f = 0;
+    for (int b = 0; b < nseq; ++b) {
+        if (cu_seqlens[b] < 0 || cu_seqlens[b + 1] < cu_seqlens[b]) return FA_ERR_INVALID_ARG;
+        const int64_t pairs = fa_visible_pairs(cu_seqlens[b + 1] - cu_seqlens[b], mask_mode,
+                                               win_l, win_r);
+        if (pairs < 0) return pairs;
+        f += (__int128)4 * D * H * pairs;
+        if (f > (__int128)INT64_MAX) return FA_ERR_TOO_LARGE;
+    }
+    return (int64_t)f;
 }
 
 // ---- new query rows against a key/value cache ---------------------------------
@@ -338,7 +427,7 @@ int decode_common(const void *q, const void *k, const void *v, void *o, float *l
     p.Sk = Sk;
     p.win_lo = pl.win_lo;
     p.win_hi = pl.win_hi;
-    p.c2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 0x1p-100f);  // as in fa_fwd
+    p.c2 = base2_scale(scale);
     p.negate_q = scale < 0.0f;
     p.tiles_per_split = pl.tiles_per_split;
     p.nsplit = pl.nsplit;

@@ -13,9 +13,9 @@ constexpr int kUnbounded = 1 << 30;
 
 // Everything a kernel needs, computed and validated on the host.
 struct FwdParams {
-    const void *q, *k, *v;  // [B, H, S, D]
-    void *o;                // [B, H, S, D]
-    float *lse;             // [B, H, S] or nullptr
+    const void *q, *k, *v;  // [B, H, S, D], or packed [T, H, D] (see row addressing)
+    void *o;                // as q
+    float *lse;             // [B, H, S] or [T, H], or nullptr
     int B, H, S;
     int n_qtiles;           // ceil(S / query rows per workgroup)
     // Key j is visible from query i iff i - win_lo <= j <= i + win_hi and j < S
@@ -32,6 +32,18 @@ struct FwdParams {
     int xcd_lists;
     int list_len;
     int group_heads;
+    // Row addressing. Row r of head h of sequence b starts at element
+    // base + r * row_stride; its LSE at index lse_base + r * lse_stride.
+    //   [B, H, S, D]:      base = (b*H + h)*S*D, row_stride = D;
+    //                      lse [B, H, S]: lse_base = (b*H + h)*S, lse_stride = 1.
+    //   packed [T, H, D]:  base = (start_b*H + h)*D, row_stride = H*D;
+    //                      lse [T, H]: lse_base = start_b*H + h, lse_stride = H.
+    // cu_seqlens != nullptr selects the packed layout: sequence b holds tokens
+    // cu_seqlens[b] .. cu_seqlens[b+1]-1 (clamped to [0, total_tokens] and to at
+    // most S rows, S then being the longest length allowed); B counts sequences.
+    int row_stride;
+    const int32_t *cu_seqlens;
+    int total_tokens;
 };
 
 // Query rows per workgroup of every kernel variant.

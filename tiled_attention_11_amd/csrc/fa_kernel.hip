@@ -80,7 +80,9 @@ template <int D> struct Geom {
     static __device__ __forceinline__ int vchunk(int q, int r) { return dev::vchunk<D>(q, r); }
 };
 
-template <typename T, int D>
+// PACKED: rows of a head lie H * D elements apart in packed [T, H, D] tensors
+// of variable-length sequences (FwdParams row addressing); otherwise [B, H, S, D].
+template <typename T, int D, bool PACKED>
 struct Kernel {
     typedef Geom<D> G;
     typedef typename Elem<T>::vec8 vec8;
@@ -117,7 +119,7 @@ struct Kernel {
     // MFMAs between an LDS operand read and its use in the MFMA phase.
     static constexpr int kDist = 8;
 
-    static __device__ __forceinline__ void make_addr(Addr &ad, int wave, int lane) {
+    static __device__ __forceinline__ void make_addr(Addr &ad, int wave, int lane, uint32_t rs) {
         const int l32 = lane & 31, g = lane >> 5;
         // DMA block b = DMA_PER_WAVE * wave + i fills tile rows
         // [b * ROWS_PER_KB, +ROWS_PER_KB); lane L lands in physical chunk
@@ -126,8 +128,8 @@ struct Kernel {
 #pragma unroll
         for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
             const int row = (G::DMA_PER_WAVE * wave + i) * G::ROWS_PER_KB + lane / G::CPR;
-            ad.kdma[i] = row * G::RB + G::kchunk(pc, row) * 16;  // XOR swizzle is its own inverse
-            ad.vdma[i] = row * G::RB + G::vchunk(pc, row) * 16;
+            ad.kdma[i] = row * rs + G::kchunk(pc, row) * 16;  // XOR swizzle is its own inverse
+            ad.vdma[i] = row * rs + G::vchunk(pc, row) * 16;
         }
         // K A operand, score block 0: row l32, logical chunk 2c + g.
 #pragma unroll
@@ -145,15 +147,18 @@ struct Kernel {
         }
     }
 
-    // Stream one K or V tile (rows k0 .. k0 + BN - 1 of the head at `h`) into
-    // the LDS slot at byte address `slot`; `off` holds this lane's source
-    // offsets (which carry the matrix's swizzle). The buffer resource starts at
-    // row k0 and ends at row S, so rows past the sequence read as zero.
-    static __device__ __forceinline__ void load_tile(const uint16_t *h, int k0, int S,
+    // Stream one K or V tile (rows k0 .. k0 + BN - 1 of the head whose row 0
+    // is at `h`, rows `rse` elements apart) into the LDS slot at byte address
+    // `slot`; `off` holds this lane's source offsets (which carry the matrix's
+    // swizzle). The buffer resource starts at row k0 and ends with row S - 1,
+    // so rows past the sequence read as zero.
+    static __device__ __forceinline__ void load_tile(const uint16_t *h, int k0, int S, int rse,
                                                      uint32_t slot,
                                                      const uint32_t (&off)[G::DMA_PER_WAVE],
                                                      int wave) {
-        const i32x4 rsrc = buffer_rsrc(h + (int64_t)k0 * D, (uint32_t)(S - k0) * G::RB);
+        const uint32_t nrec = PACKED ? (uint32_t)(S - k0 - 1) * (uint32_t)rse * 2u + G::RB
+                                     : (uint32_t)(S - k0) * G::RB;
+        const i32x4 rsrc = buffer_rsrc(h + (int64_t)k0 * rse, nrec);
 #pragma unroll
         for (int i = 0; i < G::DMA_PER_WAVE; ++i)
             dma16(rsrc, slot + (uint32_t)(G::DMA_PER_WAVE * wave + i) * 1024u, off[i]);
@@ -174,9 +179,20 @@ struct Kernel {
     struct Item {
         int bh, q0;     // head (b*H + h) and first query row
         int t_first;    // first key tile the workgroup's rows can see
-        int nt;         // number of key tiles; 0 marks "no such item"
+        int nt;         // number of key tiles; 0 marks "no more items", -1 "skip this one"
         int t_in_lo, t_in_hi;  // [t_in_lo, t_in_hi): tiles visible in full from every row
+        int S;          // PACKED: rows (queries and keys) of the item's sequence
+        int64_t base;   // PACKED: element offset of row 0 of the item's head
     };
+    // Rows of the item's sequence, and the element offset of row 0 of its head
+    // in q, k, v and o (in both layouts, offset / D indexes row 0's LSE).
+    // S_all is FwdParams::S, kept in a register by the caller.
+    static __device__ __forceinline__ int seq_len(int S_all, const Item &it) {
+        return PACKED ? it.S : S_all;
+    }
+    static __device__ __forceinline__ int64_t head_base(int S_all, const Item &it) {
+        return PACKED ? it.base : (int64_t)it.bh * S_all * D;
+    }
 
     static __device__ __forceinline__ Item item_of(const FwdParams &p, int r) {
         Item it;
@@ -189,18 +205,37 @@ struct Kernel {
             nj = (int)gridDim.x >> 3;
         }
         const int pos = r * nj + ((r & 1) ? nj - 1 - j : j);
-        if (pos >= p.list_len) {
-            it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = 0;
-            return it;
+        it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = 0;
+        if (PACKED) {
+            it.S = 0;
+            it.base = 0;
         }
+        if (pos >= p.list_len) return it;
         const int gh = p.group_heads;
         const int per_group = gh * nq;
         const int grp = pos / per_group, within = pos - grp * per_group;
         const int qt = nq - 1 - within / gh;
         const int hl = grp * gh + within % gh;
         it.bh = p.xcd_lists ? hl * 8 + x : hl;
-        const int S = p.S;
         it.q0 = qt * kBlockM;
+        int S = p.S;
+        if constexpr (PACKED) {
+            // packed sequences: clamp the offsets so that no row leaves the tensors
+            const int b = it.bh / p.H, h = it.bh - b * p.H;
+            const int ntok = p.total_tokens;
+            const int c0 = __builtin_amdgcn_readfirstlane(p.cu_seqlens[b]);
+            const int c1 = __builtin_amdgcn_readfirstlane(p.cu_seqlens[b + 1]);
+            const int start = min(max(c0, 0), ntok);
+            const int end = min(max(c1, start), ntok);
+            S = min(end - start, p.S);
+            it.base = ((int64_t)start * p.H + h) * D;
+            if (it.q0 >= S) {  // this query tile lies past the sequence
+                it.nt = -1;
+                it.bh = __builtin_amdgcn_readfirstlane(it.bh);
+                return it;
+            }
+            it.S = S;
+        }
         const int qlast = min(it.q0 + kBlockM - 1, S - 1);
         // Keys visible from any row of the item, in whole tiles; tiles outside
         // are never loaded. Every wave walks all of them: a tile hidden from a
@@ -219,7 +254,18 @@ struct Kernel {
         it.nt = __builtin_amdgcn_readfirstlane(it.nt);
         it.t_in_lo = __builtin_amdgcn_readfirstlane(it.t_in_lo);
         it.t_in_hi = __builtin_amdgcn_readfirstlane(it.t_in_hi);
+        if (PACKED) it.S = __builtin_amdgcn_readfirstlane(it.S);
         return it;
+    }
+
+    // The first item at index >= r that is not skipped (or the end marker);
+    // r is advanced to its index.
+    static __device__ __forceinline__ Item next_item(const FwdParams &p, int &r) {
+        if constexpr (!PACKED) return item_of(p, r);  // nothing is skipped
+        for (;; ++r) {
+            const Item it = item_of(p, r);
+            if (it.nt >= 0) return it;
+        }
     }
 
     // ---- phases -----------------------------------------------------------------
@@ -341,20 +387,22 @@ struct Kernel {
     // its part of the Q region. Lane L of 1 KiB block b lands in physical
     // chunk L % CPR of region row b * ROWS_PER_KB + L / CPR, so it fetches the
     // logical chunk that the K swizzle stores there.
-    static __device__ __forceinline__ void dma_q(const uint16_t *qh, int q0, int S,
+    static __device__ __forceinline__ void dma_q(const uint16_t *qh, int q0, int S, int rse,
                                                  uint32_t smem_addr, int wave, int lane) {
         const int r0 = q0 + wave * kWaveRows;
         // A wave whose rows all lie past S gets an empty resource: every read
         // returns zero and nothing past the tensor is touched.
-        const uint32_t rows = r0 < S ? (uint32_t)(S - r0) : 0u;
-        const i32x4 rsrc = buffer_rsrc(qh + (int64_t)r0 * D, rows * G::RB);
+        const uint32_t nrec = r0 >= S ? 0u
+                              : PACKED ? (uint32_t)(S - r0 - 1) * (uint32_t)rse * 2u + G::RB
+                                       : (uint32_t)(S - r0) * G::RB;
+        const i32x4 rsrc = buffer_rsrc(qh + (int64_t)r0 * rse, nrec);
         const uint32_t base = smem_addr + kQRegion + (uint32_t)(wave * kWaveRows) * G::RB;
         const int pc = lane % G::CPR;
 #pragma unroll
         for (int b = 0; b < kQBlocks; ++b) {
             const int row = b * G::ROWS_PER_KB + lane / G::CPR;
             dma16(rsrc, base + (uint32_t)b * 1024u,
-                  (uint32_t)(row * G::RB + G::kchunk(pc, row) * 16));
+                  (uint32_t)row * (uint32_t)rse * 2u + (uint32_t)(G::kchunk(pc, row) * 16));
         }
     }
     static __device__ __forceinline__ uint32_t vslot(int i) {
@@ -374,7 +422,7 @@ struct Kernel {
         const LDS char *smem;
         uint32_t smem_addr;
         const uint16_t *kh, *vh;
-        int S, t_first, ntiles, t_in_lo, t_in_hi, r0, rlast, qi, win_lo, win_hi;
+        int S, S_all, rse, t_first, ntiles, t_in_lo, t_in_hi, r0, rlast, qi, win_lo, win_hi;
         float c2;
         int g, wave, lane;
         const Addr &ad;
@@ -391,17 +439,18 @@ struct Kernel {
         // item's Q (this item's Q has been read from the Q region by then).
         __device__ __forceinline__ void dma(int i) const {
             if (i + 1 < ntiles)
-                load_tile(kh, (t_first + i + 1) * BN, S, smem_addr + kslot(kbase + i + 1),
+                load_tile(kh, (t_first + i + 1) * BN, S, rse, smem_addr + kslot(kbase + i + 1),
                           ad.kdma, wave);
             else if (i + 1 == ntiles && nx.nt > 0)
-                load_tile(static_cast<const uint16_t *>(p.k) + (int64_t)nx.bh * S * D,
-                          nx.t_first * BN, S, smem_addr + kslot(kbase + ntiles), ad.kdma, wave);
+                load_tile(static_cast<const uint16_t *>(p.k) + head_base(S_all, nx),
+                          nx.t_first * BN, seq_len(S_all, nx), rse,
+                          smem_addr + kslot(kbase + ntiles), ad.kdma, wave);
             if (i < ntiles)
-                load_tile(vh, (t_first + i) * BN, S, smem_addr + vslot(kbase + i), ad.vdma,
+                load_tile(vh, (t_first + i) * BN, S, rse, smem_addr + vslot(kbase + i), ad.vdma,
                           wave);
             if (i == 1 && nx.nt > 0)
-                dma_q(static_cast<const uint16_t *>(p.q) + (int64_t)nx.bh * S * D, nx.q0, S,
-                      smem_addr, wave, lane);
+                dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, nx), nx.q0,
+                      seq_len(S_all, nx), rse, smem_addr, wave, lane);
         }
         // M_i: O takes the rescale the softmax of tile i - 1 asked for (a wave-
         // uniform branch, rarely taken once the row maxima settle), then
@@ -557,30 +606,35 @@ struct Kernel {
         const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7
         const int l32 = lane & 31;
         const int g = lane >> 5;
-        const int S = p.S;
+        const int rse = PACKED ? p.row_stride : D;  // elements between consecutive rows of a head
+        const int S_all = p.S;  // [B, H, S, D]: every sequence's length
         const int win_lo = p.win_lo, win_hi = p.win_hi;
         const float c2 = p.c2;
         const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
         Addr ad;
-        make_addr(ad, wave, lane);
+        make_addr(ad, wave, lane, (uint32_t)rse * 2u);
 
         // The workgroup's items, one after the other. Every item ends with a
         // workgroup barrier after its last LDS read and its wait for its DMA,
         // which includes the next item's K(0) and Q: the next item starts
         // with them in LDS.
-        Item it = item_of(p, 0);  // every workgroup has at least one item
+        int r = 0;
+        Item it = next_item(p, r);
+        if (PACKED && it.nt == 0) return;  // every item of the workgroup lies past its sequence
         {
-            const uint16_t *h = static_cast<const uint16_t *>(p.k) + (int64_t)it.bh * S * D;
-            load_tile(h, it.t_first * BN, S, smem_addr + kslot(0), ad.kdma, wave);
-            dma_q(static_cast<const uint16_t *>(p.q) + (int64_t)it.bh * S * D, it.q0, S, smem_addr,
-                  wave, lane);
+            load_tile(static_cast<const uint16_t *>(p.k) + head_base(S_all, it), it.t_first * BN,
+                      seq_len(S_all, it), rse, smem_addr + kslot(0), ad.kdma, wave);
+            dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, it), it.q0,
+                  seq_len(S_all, it), rse, smem_addr, wave, lane);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
         int kbase = 0;
-        for (int r = 0; it.nt > 0; ++r) {
-            const Item nx = item_of(p, r + 1);
-            const int64_t head = (int64_t)it.bh * S * D;
+        while (it.nt > 0) {
+            ++r;
+            const Item nx = next_item(p, r);
+            const int S = seq_len(S_all, it);
+            const int64_t head = head_base(S_all, it);
             const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
             const uint16_t *vh = static_cast<const uint16_t *>(p.v) + head;
 
@@ -608,8 +662,9 @@ struct Kernel {
             st.l_run = 0.0f;
             st.alpha = 1.0f;
 
-            Loop loop{p,  smem,  smem_addr, kh,    vh, S, it.t_first, it.nt, it.t_in_lo, it.t_in_hi,
-                      r0, rlast, qi,        win_lo, win_hi, c2, g, wave, lane, ad, kbase, nx};
+            Loop loop{p,     smem,   smem_addr, kh, vh,   S,  S_all,  rse, it.t_first, it.nt,
+                      it.t_in_lo, it.t_in_hi, r0, rlast, qi, win_lo, win_hi, c2,  g, wave,
+                      lane,  ad,     kbase,     nx};
             if (grp == 0)
                 loop.template go<0>(st);
             else
@@ -619,7 +674,7 @@ struct Kernel {
             const float l_tot = sum_with_partner(st.l_run);
             if (qi < S) {
                 const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-                uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * D;
+                uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * rse;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -636,7 +691,10 @@ struct Kernel {
                     const float lse = l_tot > 0.0f
                                           ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
                                           : -INFINITY;
-                    p.lse[(int64_t)it.bh * S + qi] = lse;
+                    if (PACKED)
+                        p.lse[head / D + (int64_t)qi * p.H] = lse;
+                    else
+                        p.lse[(int64_t)it.bh * S + qi] = lse;
                 }
             }
             kbase += it.nt;
@@ -645,17 +703,18 @@ struct Kernel {
     }
 };
 
-template <typename T, int D>
+template <typename T, int D, bool PACKED>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[4 * Geom<D>::TILE_BYTES + kBlockM * Geom<D>::RB];
-    Kernel<T, D>::run(p, (LDS char *)smem);
+    Kernel<T, D, PACKED>::run(p, (LDS char *)smem);
 }
 
 template <typename T, int D>
 hipError_t launch_t(const FwdParams &p, hipStream_t stream) {
     void *args[] = {const_cast<FwdParams *>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_fwd_kernel<T, D>), dim3(p.grid),
-                           dim3(kThreads), args, 0, stream);
+    const void *fn = p.cu_seqlens ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, true>)
+                                  : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false>);
+    return hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
