@@ -156,3 +156,12 @@ def test_named_workload_sampled_rows(orc):
         got = o_bits[a + rows_i, heads]
         st = compare(got, lse[a + rows_i, heads], o_ref, lse_ref, w["dtype"])
         assert st["pass"], (a, b, st)
+
+
+def test_more_sequences_than_one_launch_holds(orc):
+    """Batches above the per-launch sequence table (1024) run as several
+    launches; every sequence still gets its own attention."""
+    rng = np.random.default_rng(80)
+    lengths = [int(x) for x in rng.integers(0, 9, 2500)]
+    say("varlen many sequences", len(lengths), "tokens", sum(lengths))
+    check(orc, lengths, 5, 2, 64, "f16", "causal", (-1, -1), seed=81)

@@ -60,17 +60,25 @@ float base2_scale(float scale) {
 // Work distribution and launch of the forward kernel, for p with everything
 // but the fields set here filled in: one workgroup per CU (each takes a whole
 // CU), each running its share of the bh * n_qtiles query tiles; see FwdParams.
+int device_cus(int *n_cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        *n_cu <= 0)
+        return FA_ERR_HIP;
+    return FA_OK;
+}
+
 int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t n_qtiles, int D, int dtype,
                         hipStream_t stream) {
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n_cu <= 0)
-        return FA_ERR_HIP;
+    int n_cu = 0;
+    if (device_cus(&n_cu) != FA_OK) return FA_ERR_HIP;
     p.n_qtiles = (int)n_qtiles;
     const uint64_t n_items = bh * n_qtiles;
     uint64_t grid = n_items < (uint64_t)n_cu ? n_items : (uint64_t)n_cu;
-    const bool xcd = bh % kNumXcd == 0 && grid >= (uint64_t)kNumXcd;
+    // Packed sequences split heads over the lists by h % 8 within every sequence.
+    const bool xcd = (p.cu_seqlens ? p.H % kNumXcd == 0 : bh % kNumXcd == 0) &&
+                     grid >= (uint64_t)kNumXcd;
     if (xcd) grid -= grid % kNumXcd;
     const uint64_t list_heads = xcd ? bh / kNumXcd : bh;
     const uint64_t nj = xcd ? grid / kNumXcd : grid;  // workgroups per list
@@ -229,7 +237,6 @@ extern "C" int fa_fwd_varlen(const void *q, const void *k, const void *v, void *
     p.v = v;
     p.o = o;
     p.lse = lse;
-    p.B = nseq;
     p.H = H;
     p.S = max_seqlen;
     p.win_lo = win_lo;
@@ -237,9 +244,16 @@ extern "C" int fa_fwd_varlen(const void *q, const void *k, const void *v, void *
     p.c2 = base2_scale(scale);
     p.negate_q = scale < 0.0f;
     p.row_stride = H * D;
-    p.cu_seqlens = cu_seqlens;
     p.total_tokens = total_tokens;
-    return plan_and_launch_fwd(p, bh, n_qtiles, D, dtype, stream);
+    // At most kMaxPackedSeqs sequences per launch (the kernel's LDS table).
+    for (int first = 0; first < nseq; first += fa::kMaxPackedSeqs) {
+        const int n = std::min(nseq - first, fa::kMaxPackedSeqs);
+        p.B = n;
+        p.cu_seqlens = cu_seqlens + first;
+        const int rc = plan_and_launch_fwd(p, (uint64_t)n * H, n_qtiles, D, dtype, stream);
+        if (rc != FA_OK) return rc;
+    }
+    return FA_OK;
 }
 
 extern "C" int64_t fa_fwd_varlen_flops(const int32_t *cu_seqlens, int nseq, int H, int D,

@@ -24,10 +24,12 @@ struct FwdParams {
     float c2;               // max(|scale| * log2(e), 2^-100): scores go to base 2 in one multiply
     int negate_q;           // scale < 0: Q's sign is flipped on load instead
     // Work distribution (see the kernel): `grid` workgroups, each running a
-    // stream of work items (query tiles). xcd_lists: B*H % 8 == 0 and grid % 8
-    // == 0, so list x (heads x, x + 8, ...) is served by workgroups w = x mod 8;
-    // otherwise one list holds every head. list_len: items per list;
-    // group_heads: heads per group within a list (divides the list's heads).
+    // stream of work items (query tiles). xcd_lists: B*H % 8 == 0 (packed: H %
+    // 8 == 0) and grid % 8 == 0, so list x (heads x, x + 8, ...) is served by
+    // workgroups w = x mod 8; otherwise one list holds every head. list_len:
+    // items per list; group_heads: heads per group within a list (divides the
+    // list's heads). Packed sequences order their lists by query tile instead
+    // and use neither.
     int grid;
     int xcd_lists;
     int list_len;
@@ -48,6 +50,9 @@ struct FwdParams {
 
 // Query rows per workgroup of every kernel variant.
 constexpr int kBlockM = 256;
+// Sequences of one packed launch (the kernel keeps a table of them in LDS);
+// the host splits larger batches over several launches.
+constexpr int kMaxPackedSeqs = 1024;
 
 // Enqueue the kernel for head dimension D and dtype (0 fp16, 1 bf16).
 hipError_t launch_fwd(const FwdParams &p, int D, int dtype, hipStream_t stream);

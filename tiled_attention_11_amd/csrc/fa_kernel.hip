@@ -194,22 +194,31 @@ struct Kernel {
         return PACKED ? it.base : (int64_t)it.bh * S_all * D;
     }
 
-    static __device__ __forceinline__ Item item_of(const FwdParams &p, int r) {
-        Item it;
-        const int nq = p.n_qtiles;
+    // The workgroup's position in its list: list x (0 without XCD lists),
+    // index j among the list's nj workgroups. Round r takes list position
+    // r * nj + j, or r * nj + nj - 1 - j in odd rounds (a snake, so that the
+    // costliest and the cheapest items of a group pair up).
+    static __device__ __forceinline__ int list_pos(const FwdParams &p, int r, int &x) {
         const int w = blockIdx.x;
-        int x = 0, j = w, nj = (int)gridDim.x;
+        int j = w, nj = (int)gridDim.x;
+        x = 0;
         if (p.xcd_lists) {
             x = w & 7;
             j = w >> 3;
             nj = (int)gridDim.x >> 3;
         }
-        const int pos = r * nj + ((r & 1) ? nj - 1 - j : j);
+        return r * nj + ((r & 1) ? nj - 1 - j : j);
+    }
+
+    // [B, H, S, D]: list position -> item. A list runs its heads in groups of
+    // group_heads, and each group's query tiles from the last to the first,
+    // the group's heads interleaved.
+    static __device__ __forceinline__ Item item_of(const FwdParams &p, int r) {
+        Item it;
+        const int nq = p.n_qtiles;
+        int x;
+        const int pos = list_pos(p, r, x);
         it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = 0;
-        if (PACKED) {
-            it.S = 0;
-            it.base = 0;
-        }
         if (pos >= p.list_len) return it;
         const int gh = p.group_heads;
         const int per_group = gh * nq;
@@ -218,24 +227,82 @@ struct Kernel {
         const int hl = grp * gh + within % gh;
         it.bh = p.xcd_lists ? hl * 8 + x : hl;
         it.q0 = qt * kBlockM;
-        int S = p.S;
-        if constexpr (PACKED) {
-            // packed sequences: clamp the offsets so that no row leaves the tensors
-            const int b = it.bh / p.H, h = it.bh - b * p.H;
-            const int ntok = p.total_tokens;
-            const int c0 = __builtin_amdgcn_readfirstlane(p.cu_seqlens[b]);
-            const int c1 = __builtin_amdgcn_readfirstlane(p.cu_seqlens[b + 1]);
-            const int start = min(max(c0, 0), ntok);
-            const int end = min(max(c1, start), ntok);
-            S = min(end - start, p.S);
-            it.base = ((int64_t)start * p.H + h) * D;
-            if (it.q0 >= S) {  // this query tile lies past the sequence
-                it.nt = -1;
-                it.bh = __builtin_amdgcn_readfirstlane(it.bh);
-                return it;
-            }
-            it.S = S;
+        finish_item(p, it, p.S);
+        return it;
+    }
+
+    // Packed sequences: the table of the launch's sequences (clamped start
+    // token and length) that every workgroup builds in LDS, and the list
+    // order. A list holds every sequence's heads h with h % 8 == x (all
+    // heads without XCD lists) and runs its items level by level: first the
+    // query tile of index n_qtiles - 1 of every (sequence, head) that has one,
+    // then tile n_qtiles - 2, ..., down to tile 0. Item costs thus fall along
+    // the list (each tile sees more keys than the one below it under causal
+    // and full masks, and the same number under a window), and the snake
+    // deals them out evenly however the lengths are mixed.
+    struct Walk {
+        int lvl;    // query tile index of the current level
+        int begin;  // list position of the level's first item
+        int count;  // items of the level
+    };
+    // Sequences with more than `lvl` query tiles (uniform).
+    static __device__ __forceinline__ int active_count(const LDS i32x2 *tab, int n, int lvl) {
+        const int lane = threadIdx.x & 63;
+        int total = 0;
+        for (int c = 0; c < n; c += 64) {
+            const bool a = c + lane < n && tab[c + lane].y > lvl * kBlockM;
+            total += __builtin_popcountll(__builtin_amdgcn_ballot_w64(a));
         }
+        return total;
+    }
+    // Index of the k-th (from 0) sequence with more than `lvl` query tiles.
+    static __device__ __forceinline__ int active_select(const LDS i32x2 *tab, int n, int lvl,
+                                                        int k) {
+        const int lane = threadIdx.x & 63;
+        for (int c = 0; c < n; c += 64) {
+            const bool a = c + lane < n && tab[c + lane].y > lvl * kBlockM;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(a);
+            const int cnt = __builtin_popcountll(m);
+            if (k < cnt) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                const uint64_t sel = __builtin_amdgcn_ballot_w64(a && (int)below == k);
+                return c + (int)__builtin_ctzll(sel);
+            }
+            k -= cnt;
+        }
+        return 0;  // not reached for k < active_count(tab, n, lvl)
+    }
+    static __device__ __forceinline__ Item packed_item(const FwdParams &p, const LDS i32x2 *tab,
+                                                       Walk &wk, int r) {
+        Item it;
+        it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = it.S = 0;
+        it.base = 0;
+        int x;
+        const int pos = list_pos(p, r, x);
+        const int hpl = p.xcd_lists ? p.H >> 3 : p.H;  // heads per sequence in a list
+        while (pos >= wk.begin + wk.count) {
+            if (wk.lvl == 0) return it;  // past the last level: no more items
+            wk.begin += wk.count;
+            --wk.lvl;
+            wk.count = hpl * active_count(tab, p.B, wk.lvl);
+        }
+        const int within = pos - wk.begin;
+        const int k = within / hpl, i = within - k * hpl;
+        const int b = active_select(tab, p.B, wk.lvl, k);
+        const int start = __builtin_amdgcn_readfirstlane(tab[b].x);
+        const int S = __builtin_amdgcn_readfirstlane(tab[b].y);
+        const int h = p.xcd_lists ? i * 8 + x : i;
+        it.bh = b * p.H + h;
+        it.q0 = wk.lvl * kBlockM;
+        it.S = S;
+        it.base = ((int64_t)start * p.H + h) * D;
+        finish_item(p, it, S);
+        return it;
+    }
+
+    // Fill in the key-tile range of an item whose bh, q0 (< S) are set.
+    static __device__ __forceinline__ void finish_item(const FwdParams &p, Item &it, int S) {
         const int qlast = min(it.q0 + kBlockM - 1, S - 1);
         // Keys visible from any row of the item, in whole tiles; tiles outside
         // are never loaded. Every wave walks all of them: a tile hidden from a
@@ -254,18 +321,15 @@ struct Kernel {
         it.nt = __builtin_amdgcn_readfirstlane(it.nt);
         it.t_in_lo = __builtin_amdgcn_readfirstlane(it.t_in_lo);
         it.t_in_hi = __builtin_amdgcn_readfirstlane(it.t_in_hi);
-        if (PACKED) it.S = __builtin_amdgcn_readfirstlane(it.S);
-        return it;
     }
 
-    // The first item at index >= r that is not skipped (or the end marker);
-    // r is advanced to its index.
-    static __device__ __forceinline__ Item next_item(const FwdParams &p, int &r) {
-        if constexpr (!PACKED) return item_of(p, r);  // nothing is skipped
-        for (;; ++r) {
-            const Item it = item_of(p, r);
-            if (it.nt >= 0) return it;
-        }
+    // The workgroup's item of round r (nt == 0: none left).
+    static __device__ __forceinline__ Item next_item(const FwdParams &p, const LDS i32x2 *tab,
+                                                     Walk &wk, int r) {
+        if constexpr (PACKED)
+            return packed_item(p, tab, wk, r);
+        else
+            return item_of(p, r);
     }
 
     // ---- phases -----------------------------------------------------------------
@@ -381,6 +445,8 @@ struct Kernel {
     // the K swizzle; wave w's rows 32w .. 32w + 31 are written (DMA) and read
     // by wave w only.
     static constexpr uint32_t kQRegion = 4 * G::TILE_BYTES;
+    // LDS byte offset of the packed-sequence table (after the Q region).
+    static constexpr uint32_t kTabOffset = kQRegion + kBlockM * G::RB;
     static constexpr int kQBlocks = kWaveRows * G::RB / 1024;  // 1 KiB DMA blocks per wave
 
     // DMA this wave's 32 rows of the item's Q (rows past S read as zero) into
@@ -614,13 +680,29 @@ struct Kernel {
         Addr ad;
         make_addr(ad, wave, lane, (uint32_t)rse * 2u);
 
+        // Packed sequences: the sequence table, with each offset clamped into
+        // [0, total_tokens] (an end below its start moved up to it) and each
+        // length to S, so that no value of cu_seqlens moves a row out of the
+        // tensors.
+        LDS i32x2 *tab = reinterpret_cast<LDS i32x2 *>(smem + kTabOffset);
+        Walk wk{p.n_qtiles, 0, 0};
+        if constexpr (PACKED) {
+            const int ntok = p.total_tokens;
+            for (int b = threadIdx.x; b < p.B; b += kThreads) {
+                const int start = min(max(p.cu_seqlens[b], 0), ntok);
+                const int end = min(max(p.cu_seqlens[b + 1], start), ntok);
+                tab[b] = i32x2{start, min(end - start, S_all)};
+            }
+            __syncthreads();
+        }
+
         // The workgroup's items, one after the other. Every item ends with a
         // workgroup barrier after its last LDS read and its wait for its DMA,
         // which includes the next item's K(0) and Q: the next item starts
         // with them in LDS.
         int r = 0;
-        Item it = next_item(p, r);
-        if (PACKED && it.nt == 0) return;  // every item of the workgroup lies past its sequence
+        Item it = next_item(p, tab, wk, r);
+        if (PACKED && it.nt == 0) return;  // every sequence is shorter than the workgroup's share
         {
             load_tile(static_cast<const uint16_t *>(p.k) + head_base(S_all, it), it.t_first * BN,
                       seq_len(S_all, it), rse, smem_addr + kslot(0), ad.kdma, wave);
@@ -632,7 +714,7 @@ struct Kernel {
         int kbase = 0;
         while (it.nt > 0) {
             ++r;
-            const Item nx = next_item(p, r);
+            const Item nx = next_item(p, tab, wk, r);
             const int S = seq_len(S_all, it);
             const int64_t head = head_base(S_all, it);
             const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
@@ -705,7 +787,8 @@ struct Kernel {
 
 template <typename T, int D, bool PACKED>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[4 * Geom<D>::TILE_BYTES + kBlockM * Geom<D>::RB];
+    __shared__ __attribute__((aligned(1024)))
+    char smem[Kernel<T, D, PACKED>::kTabOffset + (PACKED ? kMaxPackedSeqs * 8 : 0)];
     Kernel<T, D, PACKED>::run(p, (LDS char *)smem);
 }
 
