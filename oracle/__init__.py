@@ -43,6 +43,13 @@ def _bind(lib):
         _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int,
         _i64, _i64, ctypes.c_int, _ptr, _ptr, ctypes.c_int]
     lib.oracle_attention_kv.restype = ctypes.c_int
+    lib.oracle_rope_rows.argtypes = [_ptr, _i64, _i64, _ptr, _ptr, _ptr, ctypes.c_int,
+                                     ctypes.c_int, _ptr]
+    lib.oracle_rope_rows.restype = ctypes.c_int
+    lib.oracle_attention_rope_rows.argtypes = [
+        _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64, _i64,
+        ctypes.c_int, _ptr, _ptr, ctypes.c_int, _i64, _ptr, _ptr, _ptr, ctypes.c_int]
+    lib.oracle_attention_rope_rows.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [_ptr, _i64, ctypes.c_int, _ptr]
     lib.oracle_decode.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -158,6 +165,71 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_attention_kv rejected its arguments")
         return o, lse
+
+    # -- rotary position embedding --------------------------------------------
+    _ROPE_MODES = {"half": 0, "interleaved": 1}
+
+    @staticmethod
+    def _tables(cos, sin, D):
+        cos = np.ascontiguousarray(cos, dtype=np.float32)
+        sin = np.ascontiguousarray(sin, dtype=np.float32)
+        if cos.ndim != 2 or cos.shape != sin.shape or cos.shape[1] != D // 2:
+            raise ValueError("cos and sin must share one [n_pos, D/2] float32 shape")
+        return cos, sin
+
+    def rope(self, x, pos, cos, sin, mode, dtype):
+        """RoPE of the rows of ``x`` (uint16 bits, [..., D]) at positions ``pos``
+        (one per row), with [n_pos, D/2] float32 tables. ``mode``: "half" or
+        "interleaved". Returns float64 of x's shape."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        D = x.shape[-1]
+        cos, sin = self._tables(cos, sin, D)
+        n = x.size // D
+        pos = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, np.int64), (n,)))
+        if n and (pos.min() < 0 or pos.max() >= cos.shape[0]):
+            raise ValueError("a position is outside the tables")
+        out = np.empty(x.shape, dtype=np.float64)
+        rc = self.lib.oracle_rope_rows(x.ctypes.data, n, D, pos.ctypes.data, cos.ctypes.data,
+                                       sin.ctypes.data, self._ROPE_MODES[mode], _DTYPES[dtype],
+                                       out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_rope_rows rejected its arguments")
+        return out
+
+    def attention_rope_rows(self, q, k, v, dtype, scale, mask, window, cos, sin, mode,
+                            rows=None, nthreads=0):
+        """RoPE attention: q and k rows rotated at their positions 0..S-1 (tables
+        [n_pos >= S, D/2] float32), then attention. Same conventions as
+        :meth:`attention_rows`."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+        if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+            raise ValueError("q, k, v must share one [B, H, S, D] shape")
+        B, H, S, D = q.shape
+        cos, sin = self._tables(cos, sin, D)
+        if cos.shape[0] < S:
+            raise ValueError("the tables need a row per position")
+        if rows is None:
+            rows = np.arange(B * H * S, dtype=np.int64)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        m, wl, wr = self._mask_args(mask, window)
+        o = np.empty((rows.size, D), dtype=np.float64)
+        lse = np.empty(rows.size, dtype=np.float64)
+        rc = self.lib.oracle_attention_rope_rows(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, S, D, float(scale), m, wl, wr,
+            _DTYPES[dtype], cos.ctypes.data, sin.ctypes.data, self._ROPE_MODES[mode],
+            rows.size, rows.ctypes.data, o.ctypes.data, lse.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_attention_rope_rows rejected its arguments")
+        return o, lse
+
+    def attention_rope(self, q, k, v, dtype, scale, mask, window, cos, sin, mode, nthreads=0):
+        """Every row of RoPE attention: ``(o [B,H,S,D], lse [B,H,S])`` float64."""
+        B, H, S, D = q.shape
+        o, lse = self.attention_rope_rows(q, k, v, dtype, scale, mask, window, cos, sin, mode,
+                                          None, nthreads)
+        return o.reshape(B, H, S, D), lse.reshape(B, H, S)
 
     def attention_varlen(self, q, k, v, cu_seqlens, dtype, scale, mask, window=(-1, -1),
                          nthreads=0):

@@ -143,6 +143,25 @@ static int check_args(int64_t B, int64_t H, int64_t S, int64_t D, int mask_mode,
     return 0;
 }
 
+/* The scaled score of a visible pair from its dot product. */
+static double scaled(double acc, double scale)
+{
+#if ORACLE_PLANT == 1
+    (void)scale;
+    return acc;                          /* planted: scale dropped */
+#elif ORACLE_PLANT == 4
+    return -scale * acc;                 /* planted: sign flipped */
+#else
+    return scale * acc;
+#endif
+}
+
+/* Softmax of a materialised score row (S entries, -inf where hidden) and its
+ * product with the head's [S, D] value block vh: two passes over srow.
+ * orow (D doubles) is scratch owned by the caller. */
+static void finish_row(const double *srow, const uint16_t *vh, int64_t S, int64_t D,
+                       int dtype, double *orow, double *o_out, double *lse_out);
+
 /* One query row against S keys: materialise the score row, then two passes.
  * qsrc points at the query row's D values, kh and vh at the head's [S, D] key
  * and value blocks; i is the query's position in the sequence, which the mask
@@ -167,15 +186,34 @@ static void one_row(const uint16_t *qsrc, const uint16_t *kh, const uint16_t *vh
         double acc = 0.0;
         for (int64_t d = 0; d < D; ++d)
             acc += qrow[d] * decode(kh[j * D + d], dtype);
-#if ORACLE_PLANT == 1
-        srow[j] = acc;                   /* planted: scale dropped */
-#elif ORACLE_PLANT == 4
-        srow[j] = -scale * acc;          /* planted: sign flipped */
-#else
-        srow[j] = scale * acc;
-#endif
+        srow[j] = scaled(acc, scale);
     }
+    finish_row(srow, vh, S, D, dtype, orow, o_out, lse_out);
+}
 
+/* As one_row, for a query row and a key block given as fp64 values (the
+ * rotated rows of the RoPE attention below). */
+static void one_row_f64(const double *qrow, const double *kd, const uint16_t *vh, int64_t S,
+                        int64_t D, double scale, int mask_mode, int64_t wl, int64_t wr,
+                        int dtype, int64_t i, double *srow, double *orow, double *o_out,
+                        double *lse_out)
+{
+    for (int64_t j = 0; j < S; ++j) {
+        if (!oracle_visible(i, j, mask_mode, wl, wr)) {
+            srow[j] = -INFINITY;
+            continue;
+        }
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc += qrow[d] * kd[j * D + d];
+        srow[j] = scaled(acc, scale);
+    }
+    finish_row(srow, vh, S, D, dtype, orow, o_out, lse_out);
+}
+
+static void finish_row(const double *srow, const uint16_t *vh, int64_t S, int64_t D,
+                       int dtype, double *orow, double *o_out, double *lse_out)
+{
     /* Pass 1: row maximum. */
     double m = -INFINITY;
     for (int64_t j = 0; j < S; ++j)
@@ -347,6 +385,109 @@ int oracle_attention_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         free(qrow);
         free(orow);
     }
+    return failed ? -1 : 0;
+}
+
+/* Rotary position embedding (RoPE) of n_rows rows of D values.
+ * Ascend C tile-fusion page, section 9 (integration with RoPE): Q and K rows
+ * are rotated according to their position, from a cos/sin table, before the
+ * scores are formed. The page names the table but not the formula; the
+ * reading here is the usual rotary embedding: the D dimensions form D/2 pairs
+ * (a_t, b_t), and pair t of a row at position p turns by the angle whose
+ * cosine and sine are c = cos_t[p * D/2 + t], s = sin_t[p * D/2 + t]:
+ *     x'[a_t] = x[a_t] * c - x[b_t] * s,    x'[b_t] = x[b_t] * c + x[a_t] * s.
+ * Pairing mode 0 (halves): a_t = t, b_t = t + D/2. Mode 1 (interleaved):
+ * a_t = 2t, b_t = 2t + 1. Row r is at position pos[r]. Table values are taken
+ * exactly (fp32 -> fp64); everything is fp64. D must be even.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_rope_rows(const uint16_t *x, int64_t n_rows, int64_t D, const int64_t *pos,
+                     const float *cos_t, const float *sin_t, int mode, int dtype, double *out)
+{
+    if (D <= 0 || D % 2 || (mode != 0 && mode != 1)) return -1;
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+    const int64_t half = D / 2;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const uint16_t *xr = x + r * D;
+        double *yr = out + r * D;
+        for (int64_t t = 0; t < half; ++t) {
+            const int64_t a = mode == 0 ? t : 2 * t;
+            const int64_t b = mode == 0 ? t + half : 2 * t + 1;
+            const double c = (double)cos_t[pos[r] * half + t];
+            const double sn = (double)sin_t[pos[r] * half + t];
+            const double xa = decode(xr[a], dtype), xb = decode(xr[b], dtype);
+#if ORACLE_PLANT == 8
+            yr[a] = xa * c + xb * sn;            /* planted: rotation sign */
+            yr[b] = xb * c - xa * sn;
+#else
+            yr[a] = xa * c - xb * sn;
+            yr[b] = xb * c + xa * sn;
+#endif
+        }
+    }
+    return 0;
+}
+
+/* Selected rows of RoPE attention over [B,H,S,D]: every query and key row is
+ * rotated by oracle_rope_rows at its position in the sequence (0 .. S-1, from
+ * tables with at least S rows), then the attention above is taken of the
+ * rotated rows (v is not rotated). rows, o, lse and nthreads as for
+ * oracle_attention_rows. Returns 0, or -1 on a bad argument. */
+int oracle_attention_rope_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                               int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                               int mask_mode, int64_t wl, int64_t wr, int dtype,
+                               const float *cos_t, const float *sin_t, int mode,
+                               int64_t n_rows, const int64_t *rows, double *o, double *lse,
+                               int nthreads)
+{
+    if (check_args(B, H, S, D, mask_mode, dtype)) return -1;
+    if (D % 2 || (mode != 0 && mode != 1)) return -1;
+    const int64_t total_rows = B * H * S;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= total_rows) return -1;
+    if (n_rows == 0) return 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    double *kd = (double *)malloc(sizeof(double) * (size_t)(S * D));
+    if (!kd) return -1;
+    int failed = 0;
+    /* head by head: rotate the head's keys once, then its selected rows */
+    for (int64_t bh = 0; bh < B * H && !failed; ++bh) {
+        int64_t any = 0;
+        for (int64_t r = 0; r < n_rows && !any; ++r) any = rows[r] / S == bh;
+        if (!any) continue;
+        const int64_t base = bh * S * D;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+        for (int64_t j = 0; j < S; ++j) {
+            const int64_t p = j;
+            oracle_rope_rows(k + base + j * D, 1, D, &p, cos_t, sin_t, mode, dtype, kd + j * D);
+        }
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+        {
+            double *srow = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+            double *qrow = (double *)malloc(sizeof(double) * (size_t)D);
+            double *orow = (double *)malloc(sizeof(double) * (size_t)D);
+            if (!srow || !qrow || !orow) {
+                failed = 1;
+            } else {
+#pragma omp for schedule(dynamic, 4)
+                for (int64_t r = 0; r < n_rows; ++r) {
+                    if (rows[r] / S != bh) continue;
+                    const int64_t i = rows[r] % S;
+                    oracle_rope_rows(q + base + i * D, 1, D, &i, cos_t, sin_t, mode, dtype,
+                                     qrow);
+                    one_row_f64(qrow, kd, v + base, S, D, scale, mask_mode, wl, wr, dtype, i,
+                                srow, orow, o + r * D, lse + r);
+                }
+            }
+            free(srow);
+            free(qrow);
+            free(orow);
+        }
+    }
+    free(kd);
     return failed ? -1 : 0;
 }
 

@@ -160,6 +160,15 @@ def varlen_inputs(name):
     return q, k, v, cu_seqlens_of(lengths)
 
 
+def rope_tables(n_pos, D, base=10000.0):
+    """Rotary-embedding tables ``(cos, sin)``, float32 [n_pos, D/2]: pair t of a
+    row at position p turns by p * base^(-2t/D) radians (the usual frequency
+    ladder of rotary embeddings), evaluated in float64 and rounded once."""
+    t = np.arange(D // 2, dtype=np.float64)
+    ang = np.arange(n_pos, dtype=np.float64)[:, None] * base ** (-2.0 * t / D)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
 def make_decode_qkv(B, H, Sq, Sk, D, dtype, seed):
     """q [B,H,Sq,D] and the cache k, v [B,H,Sk,D]: standard normal fp32 drawn in
     the order q, k, v from one generator, each rounded once to ``dtype``."""

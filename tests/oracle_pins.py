@@ -406,6 +406,80 @@ def pin_varlen_block_diagonal_sdpa(orc):
                 assert np.isnan(o[seq < 0]).all() and np.isnan(lse[seq < 0]).all()
 
 
+def _rope_complex(xd, pos, cos, sin, mode):
+    """RoPE through complex multiplication: pair t of a row (halves: dims t and
+    t + D/2; interleaved: dims 2t and 2t + 1) read as the complex number
+    x_a + i x_b, times c + i s from the tables at the row's position."""
+    D = xd.shape[-1]
+    if mode == "half":
+        z = xd[..., : D // 2] + 1j * xd[..., D // 2:]
+    else:
+        z = xd[..., 0::2] + 1j * xd[..., 1::2]
+    w = cos.astype(np.float64)[pos] + 1j * sin.astype(np.float64)[pos]
+    z = z * w
+    out = np.empty_like(xd)
+    if mode == "half":
+        out[..., : D // 2], out[..., D // 2:] = z.real, z.imag
+    else:
+        out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
+def pin_rope_is_complex_rotation(orc):
+    """RoPE of a row equals multiplying each of its pairs, read as a complex
+    number, by cos + i sin of the row's position (random angles), in both
+    pairings; it keeps every pair's length."""
+    rng = np.random.default_rng(33)
+    for dtype in ("f16", "bf16"):
+        for D in (8, 64, 128):
+            ang = rng.uniform(-7.0, 7.0, (11, D // 2))
+            cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+            x, _, _ = make_qkv(1, 1, 20, D, dtype, seed=int(rng.integers(1 << 30)))
+            x = x[0, 0]
+            pos = rng.integers(0, 11, 20)
+            xd = _decode_ref(x, dtype)
+            for mode in ("half", "interleaved"):
+                got = orc.rope(x, pos, cos, sin, mode, dtype)
+                ref = _rope_complex(xd, pos, cos, sin, mode)
+                assert np.max(np.abs(got - ref)) < 1e-12, (dtype, D, mode)
+                assert abs(np.sum(got ** 2) - np.sum(xd ** 2)) < 1e-6 * np.sum(xd ** 2) + 1e-9
+
+
+def pin_rope_attention_sdpa(orc):
+    """RoPE attention equals torch's CPU fp64 scaled_dot_product_attention of
+    the q and k rows rotated (by complex multiplication) at their positions,
+    with the mask, and torch.logsumexp; tables from the usual frequency ladder."""
+    from synth import rope_tables
+    for dtype in ("f16", "bf16"):
+        for mode in ("half", "interleaved"):
+            S, D = 37, 16
+            q, k, v = make_qkv(1, 2, S, D, dtype, seed=34)
+            cos, sin = rope_tables(S + 5, D, base=100.0)
+            pos = np.arange(S)
+            qd = torch.from_numpy(_rope_complex(_decode_ref(q, dtype), pos, cos, sin, mode))
+            kd = torch.from_numpy(_rope_complex(_decode_ref(k, dtype), pos, cos, sin, mode))
+            vd = torch.from_numpy(_decode_ref(v, dtype))
+            for mask, window in MASK_CASES:
+                bm = torch.from_numpy(_bool_mask_kv(S, S, mask, window))
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qd, kd, vd, attn_mask=bm, scale=0.3).numpy()
+                sc = torch.matmul(qd, kd.transpose(-1, -2)) * 0.3
+                lse_ref = torch.logsumexp(sc.masked_fill(~bm, float("-inf")), dim=-1).numpy()
+                o, lse = orc.attention_rope(q, k, v, dtype, 0.3, mask, window, cos, sin, mode)
+                assert np.max(np.abs(o - ref)) < 1e-12, (dtype, mode, mask, window)
+                assert np.max(np.abs(lse - lse_ref)) < 1e-12, (dtype, mode, mask, window)
+
+
+def pin_rope_zero_angle_is_plain_attention(orc):
+    """Tables of angle 0 (cos 1, sin 0) give the plain attention exactly."""
+    q, k, v = make_qkv(2, 2, 50, 32, "f16", seed=35)
+    cos, sin = np.ones((50, 16), np.float32), np.zeros((50, 16), np.float32)
+    for mode in ("half", "interleaved"):
+        o, lse = orc.attention_rope(q, k, v, "f16", 0.2, "causal", (-1, -1), cos, sin, mode)
+        o0, lse0 = orc.attention(q, k, v, "f16", 0.2, "causal")
+        assert np.array_equal(o, o0) and np.array_equal(lse, lse0)
+
+
 def pin_kv_is_the_tail_of_the_square_case(orc):
     """New rows at the end of a sequence give the last rows of the square
     problem whose query rows end with them (any earlier query rows)."""
@@ -456,4 +530,7 @@ ALL_PINS = [
     pin_kv_is_the_tail_of_the_square_case,
     pin_kv_uniform_weights,
     pin_varlen_block_diagonal_sdpa,
+    pin_rope_is_complex_rotation,
+    pin_rope_attention_sdpa,
+    pin_rope_zero_angle_is_plain_attention,
 ]
