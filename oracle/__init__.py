@@ -43,6 +43,8 @@ def _bind(lib):
         _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int,
         _i64, _i64, ctypes.c_int, _ptr, _ptr, ctypes.c_int]
     lib.oracle_attention_kv.restype = ctypes.c_int
+    lib.oracle_round.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.oracle_round.restype = ctypes.c_double
     lib.oracle_rope_rows.argtypes = [_ptr, _i64, _i64, _ptr, _ptr, _ptr, ctypes.c_int,
                                      ctypes.c_int, _ptr]
     lib.oracle_rope_rows.restype = ctypes.c_int
@@ -167,7 +169,7 @@ class Oracle:
         return o, lse
 
     # -- rotary position embedding --------------------------------------------
-    _ROPE_MODES = {"half": 0, "interleaved": 1}
+    _ROPE_MODES = {"halves": 0, "interleaved": 1}
 
     @staticmethod
     def _tables(cos, sin, D):
@@ -177,9 +179,14 @@ class Oracle:
             raise ValueError("cos and sin must share one [n_pos, D/2] float32 shape")
         return cos, sin
 
+    def round_to(self, x, dtype):
+        """Nearest ``dtype`` value of each float64 in ``x`` (ties to even), as float64."""
+        return np.array([self.lib.oracle_round(float(t), _DTYPES[dtype])
+                         for t in np.asarray(x, np.float64).ravel()]).reshape(np.shape(x))
+
     def rope(self, x, pos, cos, sin, mode, dtype):
         """RoPE of the rows of ``x`` (uint16 bits, [..., D]) at positions ``pos``
-        (one per row), with [n_pos, D/2] float32 tables. ``mode``: "half" or
+        (one per row), with [n_pos, D/2] float32 tables. ``mode``: "halves" or
         "interleaved". Returns float64 of x's shape."""
         x = np.ascontiguousarray(x, dtype=np.uint16)
         D = x.shape[-1]
@@ -199,8 +206,8 @@ class Oracle:
     def attention_rope_rows(self, q, k, v, dtype, scale, mask, window, cos, sin, mode,
                             rows=None, nthreads=0):
         """RoPE attention: q and k rows rotated at their positions 0..S-1 (tables
-        [n_pos >= S, D/2] float32), then attention. Same conventions as
-        :meth:`attention_rows`."""
+        [n_pos >= S, D/2] float32) and rounded to ``dtype``, then attention.
+        Same conventions as :meth:`attention_rows`."""
         q = np.ascontiguousarray(q, dtype=np.uint16)
         k = np.ascontiguousarray(k, dtype=np.uint16)
         v = np.ascontiguousarray(v, dtype=np.uint16)

@@ -90,6 +90,30 @@ static double decode(uint16_t x, int dtype)
     return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(x) : oracle_f16_to_f64(x);
 }
 
+/* The element type's value nearest to x, ties to the even significand
+ * (round-to-nearest-even), as a double. A binary format with p significand
+ * bits (11 for binary16, 8 for bfloat16) and smallest normal 2^emin (2^-14,
+ * 2^-126) spaces its values 2^(e - p) apart where x = m 2^e, 0.5 <= |m| < 1,
+ * and never closer than its subnormal step 2^(emin - p + 1); a value past the
+ * largest finite one (65504, or (2 - 2^-7) 2^127) after rounding is +-inf. */
+double oracle_round(double x, int dtype)
+{
+    const int p = dtype == ORACLE_BF16 ? 8 : 11;
+    const int emin = dtype == ORACLE_BF16 ? -126 : -14;
+    const double maxf = dtype == ORACLE_BF16 ? ldexp(2.0 - ldexp(1.0, -7), 127) : 65504.0;
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    int e;
+    frexp(x, &e);
+    const int q = (e - p > emin - p + 1) ? e - p : emin - p + 1;
+#if ORACLE_PLANT == 9
+    const double r = ldexp(round(ldexp(x, -q)), q);      /* planted: ties away from zero */
+#else
+    const double r = ldexp(nearbyint(ldexp(x, -q)), q);  /* exact scaling; RNE */
+#endif
+    if (fabs(r) > maxf) return x > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
 /* Is key j visible from query i?
  *   full:   always (catlass article, "usage": no mask).
  *   causal: j <= i. The Ascend C tile-fusion page, section 4.2, masks a key
@@ -398,7 +422,8 @@ int oracle_attention_kv(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  *     x'[a_t] = x[a_t] * c - x[b_t] * s,    x'[b_t] = x[b_t] * c + x[a_t] * s.
  * Pairing mode 0 (halves): a_t = t, b_t = t + D/2. Mode 1 (interleaved):
  * a_t = 2t, b_t = 2t + 1. Row r is at position pos[r]. Table values are taken
- * exactly (fp32 -> fp64); everything is fp64. D must be even.
+ * exactly (fp32 -> fp64); everything is fp64 and out is not rounded. D must
+ * be even.
  * Returns 0, or -1 on a bad argument. */
 int oracle_rope_rows(const uint16_t *x, int64_t n_rows, int64_t D, const int64_t *pos,
                      const float *cos_t, const float *sin_t, int mode, int dtype, double *out)
@@ -429,9 +454,13 @@ int oracle_rope_rows(const uint16_t *x, int64_t n_rows, int64_t D, const int64_t
 
 /* Selected rows of RoPE attention over [B,H,S,D]: every query and key row is
  * rotated by oracle_rope_rows at its position in the sequence (0 .. S-1, from
- * tables with at least S rows), then the attention above is taken of the
- * rotated rows (v is not rotated). rows, o, lse and nthreads as for
- * oracle_attention_rows. Returns 0, or -1 on a bad argument. */
+ * tables with at least S rows) and each rotated value rounded to the element
+ * type (oracle_round), then the attention above is taken of those rows (v is
+ * not rotated). Reading: the tile-fusion page, section 9, applies the
+ * rotation as the Q and K tiles are loaded for the matrix unit, which takes
+ * the element type (section 10: fp16 inputs, fp32 accumulation), so the
+ * rotated rows enter QK^T in the element type. rows, o, lse and nthreads as
+ * for oracle_attention_rows. Returns 0, or -1 on a bad argument. */
 int oracle_attention_rope_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                int64_t B, int64_t H, int64_t S, int64_t D, double scale,
                                int mask_mode, int64_t wl, int64_t wr, int dtype,
@@ -463,6 +492,7 @@ int oracle_attention_rope_rows(const uint16_t *q, const uint16_t *k, const uint1
         for (int64_t j = 0; j < S; ++j) {
             const int64_t p = j;
             oracle_rope_rows(k + base + j * D, 1, D, &p, cos_t, sin_t, mode, dtype, kd + j * D);
+            for (int64_t d = 0; d < D; ++d) kd[j * D + d] = oracle_round(kd[j * D + d], dtype);
         }
 #pragma omp parallel num_threads(nthreads) reduction(| : failed)
         {
@@ -478,6 +508,7 @@ int oracle_attention_rope_rows(const uint16_t *q, const uint16_t *k, const uint1
                     const int64_t i = rows[r] % S;
                     oracle_rope_rows(q + base + i * D, 1, D, &i, cos_t, sin_t, mode, dtype,
                                      qrow);
+                    for (int64_t d = 0; d < D; ++d) qrow[d] = oracle_round(qrow[d], dtype);
                     one_row_f64(qrow, kd, v + base, S, D, scale, mask_mode, wl, wr, dtype, i,
                                 srow, orow, o + r * D, lse + r);
                 }

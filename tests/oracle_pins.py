@@ -411,14 +411,14 @@ def _rope_complex(xd, pos, cos, sin, mode):
     t + D/2; interleaved: dims 2t and 2t + 1) read as the complex number
     x_a + i x_b, times c + i s from the tables at the row's position."""
     D = xd.shape[-1]
-    if mode == "half":
+    if mode == "halves":
         z = xd[..., : D // 2] + 1j * xd[..., D // 2:]
     else:
         z = xd[..., 0::2] + 1j * xd[..., 1::2]
     w = cos.astype(np.float64)[pos] + 1j * sin.astype(np.float64)[pos]
     z = z * w
     out = np.empty_like(xd)
-    if mode == "half":
+    if mode == "halves":
         out[..., : D // 2], out[..., D // 2:] = z.real, z.imag
     else:
         out[..., 0::2], out[..., 1::2] = z.real, z.imag
@@ -438,26 +438,62 @@ def pin_rope_is_complex_rotation(orc):
             x = x[0, 0]
             pos = rng.integers(0, 11, 20)
             xd = _decode_ref(x, dtype)
-            for mode in ("half", "interleaved"):
+            for mode in ("halves", "interleaved"):
                 got = orc.rope(x, pos, cos, sin, mode, dtype)
                 ref = _rope_complex(xd, pos, cos, sin, mode)
                 assert np.max(np.abs(got - ref)) < 1e-12, (dtype, D, mode)
                 assert abs(np.sum(got ** 2) - np.sum(xd ** 2)) < 1e-6 * np.sum(xd ** 2) + 1e-9
 
 
+def pin_round_to_element_type(orc):
+    """Rounding to fp16 matches numpy's float64 -> float16 conversion (round to
+    nearest even, subnormals, overflow); rounding to bf16 matches torch's
+    float32 -> bfloat16 conversion on float32 values, and exact halfway cases
+    and their neighbours 2^-40 away round to even / to the nearer value."""
+    rng = np.random.default_rng(36)
+    x = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-9, 6, 3000),
+                        [0.0, -0.0, 65504.0, 65519.9, 65520.0, -7e4, 2.0 ** -25, 3 * 2.0 ** -26,
+                         2.0 ** -24 * 1.5, 1e-9]])
+    got = orc.round_to(x, "f16")
+    ref = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref)
+    x32 = (rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000)).astype(np.float32)
+    got = orc.round_to(x32.astype(np.float64), "bf16")
+    ref = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, ref)
+    # bf16 values 1 + k/128 are spaced 2^-7 apart near 1: halfway cases round to even
+    for k in range(0, 10):
+        lo = 1.0 + k / 128.0
+        mid = lo + 2.0 ** -8
+        even = lo if k % 2 == 0 else lo + 2.0 ** -7
+        assert orc.round_to([mid], "bf16")[0] == even
+        assert orc.round_to([mid + 2.0 ** -40], "bf16")[0] == lo + 2.0 ** -7
+        assert orc.round_to([mid - 2.0 ** -40], "bf16")[0] == lo
+
+
 def pin_rope_attention_sdpa(orc):
     """RoPE attention equals torch's CPU fp64 scaled_dot_product_attention of
-    the q and k rows rotated (by complex multiplication) at their positions,
-    with the mask, and torch.logsumexp; tables from the usual frequency ladder."""
+    the q and k rows rotated (by complex multiplication) at their positions and
+    rounded to the element type (numpy for fp16, the oracle's pinned rounding
+    for bf16), with the mask, and torch.logsumexp; tables from the usual
+    frequency ladder."""
     from synth import rope_tables
     for dtype in ("f16", "bf16"):
-        for mode in ("half", "interleaved"):
+        for mode in ("halves", "interleaved"):
             S, D = 37, 16
             q, k, v = make_qkv(1, 2, S, D, dtype, seed=34)
             cos, sin = rope_tables(S + 5, D, base=100.0)
             pos = np.arange(S)
-            qd = torch.from_numpy(_rope_complex(_decode_ref(q, dtype), pos, cos, sin, mode))
-            kd = torch.from_numpy(_rope_complex(_decode_ref(k, dtype), pos, cos, sin, mode))
+
+            def rounded(x):
+                if dtype == "f16":
+                    return x.astype(np.float16).astype(np.float64)
+                return orc.round_to(x, "bf16")
+
+            qd = torch.from_numpy(rounded(_rope_complex(_decode_ref(q, dtype), pos, cos, sin,
+                                                        mode)))
+            kd = torch.from_numpy(rounded(_rope_complex(_decode_ref(k, dtype), pos, cos, sin,
+                                                        mode)))
             vd = torch.from_numpy(_decode_ref(v, dtype))
             for mask, window in MASK_CASES:
                 bm = torch.from_numpy(_bool_mask_kv(S, S, mask, window))
@@ -474,7 +510,7 @@ def pin_rope_zero_angle_is_plain_attention(orc):
     """Tables of angle 0 (cos 1, sin 0) give the plain attention exactly."""
     q, k, v = make_qkv(2, 2, 50, 32, "f16", seed=35)
     cos, sin = np.ones((50, 16), np.float32), np.zeros((50, 16), np.float32)
-    for mode in ("half", "interleaved"):
+    for mode in ("halves", "interleaved"):
         o, lse = orc.attention_rope(q, k, v, "f16", 0.2, "causal", (-1, -1), cos, sin, mode)
         o0, lse0 = orc.attention(q, k, v, "f16", 0.2, "causal")
         assert np.array_equal(o, o0) and np.array_equal(lse, lse0)
@@ -530,6 +566,7 @@ ALL_PINS = [
     pin_kv_is_the_tail_of_the_square_case,
     pin_kv_uniform_weights,
     pin_varlen_block_diagonal_sdpa,
+    pin_round_to_element_type,
     pin_rope_is_complex_rotation,
     pin_rope_attention_sdpa,
     pin_rope_zero_angle_is_plain_attention,
