@@ -33,6 +33,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["tiled_attention_11_amd/csrc/fa_kernel.hip",
                   "tiled_attention_11_amd/csrc/fa_internal.h",
                   "tiled_attention_11_amd/csrc/fa_device.h"]
+ROPE_SOURCES = KERNEL_SOURCES + ["tiled_attention_11_amd/csrc/fa_rope.hip"]
 DECODE_SOURCES = ["tiled_attention_11_amd/csrc/fa_decode.hip",
                   "tiled_attention_11_amd/csrc/fa_internal.h",
                   "tiled_attention_11_amd/csrc/fa_device.h"]
@@ -88,14 +89,23 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, seconds):
     total = B * H * S
     rng = np.random.default_rng(1234)
     args = (q, k, v, w["dtype"], w["scale"], w["mask"], w["window"])
+    if w.get("rope"):
+        import synth
+        cos, sin = synth.rope_tables(S, D, w["rope_base"])
+
+        def rows_of(rows):
+            return orc.attention_rope_rows(*args, cos, sin, w["rope"], rows=rows)
+    else:
+        def rows_of(rows):
+            return orc.attention_rows(*args, rows=rows)
     probe = rng.choice(total, size=min(64, total), replace=False)
     t0 = time.perf_counter()
-    orc.attention_rows(*args, rows=probe)
+    rows_of(probe)
     dt = max(time.perf_counter() - t0, 1e-4)
     n = int(min(total, max(64, len(probe) * seconds / dt)))
     rows = np.sort(rng.choice(total, size=n, replace=False))
     t0 = time.perf_counter()
-    o_ref, lse_ref = orc.attention_rows(*args, rows=rows)
+    o_ref, lse_ref = rows_of(rows)
     dt = time.perf_counter() - t0
     pairs = int(visible_per_row(S, w["mask"], w["window"], rows % S).sum())
     flops = 4 * D * pairs
@@ -422,12 +432,21 @@ def main():
     tq, tk, tv = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev) for x in (q, k, v))
     out = torch.empty_like(tq)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    rope = w.get("rope")
+    if rope:
+        cos, sin = synth.rope_tables(S, D, w["rope_base"])
+        tcos, tsin = torch.from_numpy(cos).to(dev), torch.from_numpy(sin).to(dev)
+        k_rot = torch.empty_like(tk)
     print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
 
     def step():
-        fa.forward(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
-                   lse=lse)
+        if rope:
+            fa.forward_rope(tq, tk, tv, tcos, tsin, mode=rope, k_rot=k_rot, scale=w["scale"],
+                            mask=w["mask"], window=(wl, wr), out=out, lse=lse)
+        else:
+            fa.forward(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
+                       lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -456,10 +475,13 @@ def main():
 
     flops = fa.fa_fwd_flops(B, H, S, D, fa._mask_code(w["mask"]), wl, wr)
     tflops = flops / avg_s / 1e12
-    traffic = counted_traffic(name)
+    traffic = counted_traffic(name, sources=ROPE_SOURCES if w.get("rope") else None)
 
     result = {
-        "metric": "attention fwd TFLOP/s and % of fp16 MFMA peak, B4 H32 S4096 D128 causal",
+        "metric": ("attention fwd TFLOP/s and % of fp16 MFMA peak, B4 H32 S4096 D128 causal"
+                   if name == synth.HEADLINE else
+                   "attention fwd" + (" with RoPE of q and k" if rope else "")
+                   + f" TFLOP/s and % of fp16 MFMA peak, {name}"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -474,7 +496,10 @@ def main():
         "config": {
             "workload": (f"{name}: B={B} H={H} S={S} D={D} {dtype} {w['mask']}"
                          + (f" window=({wl},{wr})" if w["mask"] == "window" else "")
-                         + f" scale={w['scale']:.6g}"),
+                         + f" scale={w['scale']:.6g}"
+                         + (f", RoPE of q and k ({rope}, base {w['rope_base']:g}): one fa_rope "
+                            "launch over k + the forward with q rotated in registers"
+                            if rope else "")),
             "B": B, "H": H, "S": S, "D": D, "mask": w["mask"], "window": [wl, wr],
             "flops_per_step": flops,
         },

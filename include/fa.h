@@ -54,6 +54,13 @@ typedef enum {
     FA_DTYPE_BF16 = 1  /* bfloat16 */
 } fa_dtype;
 
+/* Pairings of the rotary embedding (fa_rope, fa_fwd_rope): dims (t, t + D/2)
+ * or (2t, 2t + 1) form pair t, for t = 0 .. D/2 - 1. */
+typedef enum {
+    FA_ROPE_HALVES = 0,
+    FA_ROPE_INTERLEAVED = 1
+} fa_rope_mode;
+
 /* Return codes. Every code except FA_ERR_HIP is returned before anything is
  * enqueued or written. */
 typedef enum {
@@ -163,6 +170,52 @@ int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *l
  */
 int64_t fa_fwd_varlen_flops(const int32_t *cu_seqlens, int nseq, int H, int D,
                             int mask_mode, int win_l, int win_r);
+
+/*
+ * fa_rope -- rotary position embedding (RoPE) of a [B, H, S, D] tensor: pair
+ * t of row s of every head (see fa_rope_mode) turns by the angle whose cosine
+ * and sine are cos_table[s * D/2 + t] and sin_table[s * D/2 + t]:
+ *     y[a] = x[a] c - x[b] s,   y[b] = x[b] c + x[a] s,
+ * computed in fp32 from the exact inputs and rounded once (RNE) to `dtype`.
+ * Defining passage: Ascend C FlashAttention-2 tile-fusion page
+ * (ascendai.csdn.net), section 9 (RoPE applied to Q and K from a cos/sin
+ * table), read as the usual rotary embedding.
+ *
+ * x, y        device pointers, contiguous [B, H, S, D] of `dtype`, 16-byte
+ *             aligned; y may be x (in place), otherwise they must not overlap.
+ * cos_table, sin_table
+ *             device pointers to fp32 [n_pos, D/2] (row = position), 16-byte
+ *             aligned, n_pos >= S; read only; must not overlap y.
+ * rope_mode   fa_rope_mode. B, H, S >= 0 (B*H*S == 0: nothing done); D 64 or
+ *             128; dtype, stream as for fa_fwd.
+ * Limits: B*H*S*D/16 < 2^31. Returns FA_OK or a negative fa_status.
+ */
+int fa_rope(const void *x, void *y, const float *cos_table, const float *sin_table,
+            int n_pos, int rope_mode, int B, int H, int S, int D, int dtype,
+            hipStream_t stream);
+
+/*
+ * fa_fwd_rope -- fa_fwd of the rotary-embedded q and k: row i of q and of k
+ * turned as fa_rope does at position i, then the attention (v unrotated).
+ * Defining passage: the tile-fusion page, section 9, which fuses the rotation
+ * into the loads of the Q and K tiles. Here the rotation of each query row is
+ * applied in registers as the row enters the kernel; k is rotated once, by
+ * fa_rope, into k_rot (each key tile is streamed by several query tiles, so
+ * rotating it on every load would repeat the work) and the attention reads
+ * k_rot. The rotated keys are the ones a key/value cache stores.
+ *
+ * k_rot       device pointer, [B, H, S, D] of `dtype`, 16-byte aligned: receives
+ *             the rotated k; may be k itself (rotated in place), otherwise must
+ *             not overlap k; must not overlap q, v, o, lse or the tables.
+ * cos_table, sin_table, n_pos, rope_mode  as for fa_rope (n_pos >= S).
+ * Every other argument, and the arithmetic of the attention, as for fa_fwd;
+ * the rotated query rows are rounded to `dtype` before QK^T, as the rotated
+ * keys are. All checks run before anything is enqueued.
+ */
+int fa_fwd_rope(const void *q, const void *k, const void *v, void *o, float *lse,
+                void *k_rot, const float *cos_table, const float *sin_table, int n_pos,
+                int rope_mode, int B, int H, int S, int D, float scale, int mask_mode,
+                int win_l, int win_r, int dtype, hipStream_t stream);
 
 /*
  * fa_decode -- attention of Sq new query rows against a key/value cache

@@ -38,6 +38,11 @@ WORKLOADS = {
                                window=(1024, 0), scale=128 ** -0.5, seed=3),
     "b4h32s4096_win1000": dict(B=4, H=32, S=4096, D=128, dtype="f16", mask="window",
                                window=(1000, 0), scale=128 ** -0.5, seed=3),
+    # the headline shape with rotary embedding of q and k (pairs of halves,
+    # the usual 10000 frequency base; tables from rope_tables)
+    "b4h32s4096_causal_rope": dict(B=4, H=32, S=4096, D=128, dtype="f16", mask="causal",
+                                   window=(-1, -1), scale=128 ** -0.5, seed=3, rope="halves",
+                                   rope_base=10000.0),
     "long_bf16_outliers": dict(B=1, H=64, S=16384, D=128, dtype="bf16", mask="causal",
                                window=(-1, -1), scale=128 ** -0.5, seed=5,
                                outlier_frac=0.01, outlier_scale=20.0),

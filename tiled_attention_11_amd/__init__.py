@@ -2,12 +2,13 @@
 
 A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
 ``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops``, ``fa_fwd_varlen``,
-``fa_fwd_varlen_flops``, ``fa_decode``, ``fa_decode_workspace_bytes``,
-``fa_decode_flops``, ``fa_decode_paged``, ``fa_decode_paged_workspace_bytes`` and
-``fa_strerror`` carry the C names and arguments (marshalling only).
-``forward``, ``forward_varlen``, ``decode`` and ``decode_paged`` are the
-convenience entries for torch tensors: torch supplies device memory and the
-stream; every step of the computation runs in the library's HIP kernels.
+``fa_fwd_varlen_flops``, ``fa_rope``, ``fa_fwd_rope``, ``fa_decode``,
+``fa_decode_workspace_bytes``, ``fa_decode_flops``, ``fa_decode_paged``,
+``fa_decode_paged_workspace_bytes`` and ``fa_strerror`` carry the C names and
+arguments (marshalling only). ``forward``, ``forward_varlen``, ``rope``,
+``forward_rope``, ``decode`` and ``decode_paged`` are the convenience entries
+for torch tensors: torch supplies device memory and the stream; every step of
+the computation runs in the library's HIP kernels.
 There is no fallback: if the library is missing, importing this package
 raises.
 """
@@ -18,14 +19,17 @@ import os
 __all__ = [
     "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
     "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
-    "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
-    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "forward_varlen", "decode",
+    "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_rope", "fa_fwd_rope", "FA_ROPE_HALVES",
+    "FA_ROPE_INTERLEAVED", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
+    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "forward_varlen", "rope", "forward_rope", "decode",
     "decode_paged",
     "lib_path", "library",
 ]
 
 FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_WINDOW = 0, 1, 2
 FA_DTYPE_FP16, FA_DTYPE_BF16 = 0, 1
+FA_ROPE_HALVES, FA_ROPE_INTERLEAVED = 0, 1
+_ROPE_MODES = {"halves": FA_ROPE_HALVES, "interleaved": FA_ROPE_INTERLEAVED}
 _MASKS = {"full": FA_MASK_FULL, "causal": FA_MASK_CAUSAL, "window": FA_MASK_WINDOW}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -63,6 +67,11 @@ def _load():
     lib.fa_fwd_varlen.restype = ci
     lib.fa_fwd_varlen_flops.argtypes = [ctypes.POINTER(ctypes.c_int32), ci, ci, ci, ci, ci, ci]
     lib.fa_fwd_varlen_flops.restype = i64
+    lib.fa_rope.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp]
+    lib.fa_rope.restype = ci
+    lib.fa_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
+                                ctypes.c_float, ci, ci, ci, ci, vp]
+    lib.fa_fwd_rope.restype = ci
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci,
                               ci, ci, vp, i64, vp]
     lib.fa_decode.restype = ci
@@ -124,6 +133,18 @@ def fa_fwd_varlen_flops(cu_seqlens, H, D, mask_mode, win_l=-1, win_r=-1):
         raise ValueError("cu_seqlens needs at least one entry")
     arr = (ctypes.c_int32 * (n + 1))(*[int(x) for x in cu_seqlens])
     return _lib.fa_fwd_varlen_flops(arr, n, H, D, mask_mode, win_l, win_r)
+
+
+def fa_rope(x, y, cos_table, sin_table, n_pos, rope_mode, B, H, S, D, dtype, stream):
+    """Call ``fa_rope`` with raw device addresses (ints); return its status."""
+    return _lib.fa_rope(x, y, cos_table, sin_table, n_pos, rope_mode, B, H, S, D, dtype, stream)
+
+
+def fa_fwd_rope(q, k, v, o, lse, k_rot, cos_table, sin_table, n_pos, rope_mode, B, H, S, D,
+                scale, mask_mode, win_l, win_r, dtype, stream):
+    """Call ``fa_fwd_rope`` with raw device addresses (ints); return its status."""
+    return _lib.fa_fwd_rope(q, k, v, o, lse, k_rot, cos_table, sin_table, n_pos, rope_mode, B,
+                            H, S, D, scale, mask_mode, win_l, win_r, dtype, stream)
 
 
 def fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
@@ -266,6 +287,100 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, *, scale=None, mask="full",
     if status != 0:
         raise FaError(status, "fa_fwd_varlen")
     return out, lse
+
+
+def _rope_code(mode):
+    if isinstance(mode, int):
+        return mode
+    try:
+        return _ROPE_MODES[mode]
+    except KeyError:
+        raise ValueError(f"rope mode must be one of {sorted(_ROPE_MODES)}, got {mode!r}") from None
+
+
+def _check_tables(cos, sin, D, x):
+    import torch
+    if (cos.dim() != 2 or cos.shape != sin.shape or cos.shape[1] != D // 2
+            or cos.dtype != torch.float32 or sin.dtype != torch.float32
+            or cos.device != x.device or sin.device != x.device
+            or not cos.is_contiguous() or not sin.is_contiguous()):
+        raise ValueError("cos and sin must be contiguous float32 [n_pos, D/2] tensors on the "
+                         "tensors' device")
+
+
+def rope(x, cos, sin, *, mode="halves", out=None, stream=None):
+    """Rotary embedding of a contiguous [B, H, S, D] float16/bfloat16 tensor:
+    row s of every head turns by the angles of row s of ``cos``/``sin``
+    (float32 [n_pos >= S, D/2]). ``out`` may be ``x`` (in place)."""
+    import torch
+
+    if x.dim() != 4 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, S, D] tensor on a GPU")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    B, H, S, D = x.shape
+    _check_tables(cos, sin, D, x)
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    dtype = FA_DTYPE_FP16 if x.dtype == torch.float16 else FA_DTYPE_BF16
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        status = fa_rope(x.data_ptr(), out.data_ptr(), cos.data_ptr(), sin.data_ptr(),
+                         cos.shape[0], _rope_code(mode), B, H, S, D, dtype, stream)
+    if status != 0:
+        raise FaError(status, "fa_rope")
+    return out
+
+
+def forward_rope(q, k, v, cos, sin, *, mode="halves", k_rot=None, scale=None, mask="full",
+                 window=(-1, -1), out=None, lse=None, return_lse=True, stream=None):
+    """``forward`` of the rotary-embedded q and k (row i of each turned by row i
+    of ``cos``/``sin``). The rotated keys are written to ``k_rot`` (allocated
+    when not given; may be ``k`` to rotate in place). Returns ``(o, lse, k_rot)``."""
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, S, D] shape")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S, D = q.shape
+    _check_tables(cos, sin, D, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if k_rot is None:
+        k_rot = torch.empty_like(k)
+    elif k_rot.shape != k.shape or k_rot.dtype != k.dtype or k_rot.device != k.device or not k_rot.is_contiguous():
+        raise ValueError("k_rot must be a contiguous tensor like k")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, S) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor on q's device")
+    wl, wr = window
+    dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        status = fa_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, k_rot.data_ptr(),
+                             cos.data_ptr(), sin.data_ptr(), cos.shape[0], _rope_code(mode),
+                             B, H, S, D, float(scale), _mask_code(mask), int(wl), int(wr), dtype,
+                             stream)
+    if status != 0:
+        raise FaError(status, "fa_fwd_rope")
+    return out, lse, k_rot
 
 
 def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse=None,

@@ -133,9 +133,21 @@ extern "C" const char *fa_strerror(int status) {
     }
 }
 
-extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
-                      int B, int H, int S, int D, float scale, int mask_mode, int win_l,
-                      int win_r, int dtype, hipStream_t stream) {
+namespace {
+
+// Rotary-embedding arguments of fa_fwd_rope (checked by fwd_core before
+// anything is enqueued).
+struct RopeArgs {
+    const void *k_in;  // k before rotation; the forward reads k_rot
+    void *k_rot;
+    const float *cos, *sin;
+    int n_pos, mode;
+};
+
+// fa_fwd, and fa_fwd_rope when rope != nullptr (k is then the rotated buffer).
+int fwd_core(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+             int S, int D, float scale, int mask_mode, int win_l, int win_r, int dtype,
+             hipStream_t stream, const RopeArgs *rope) {
     // ---- scalar arguments -------------------------------------------------
     if (B < 0 || H < 0 || S < 0) return FA_ERR_INVALID_ARG;
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
@@ -168,8 +180,43 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
     if (lse && (overlaps(pl, lbytes, pq, nbytes) || overlaps(pl, lbytes, pk, nbytes) ||
                 overlaps(pl, lbytes, pv, nbytes) || overlaps(pl, lbytes, po, nbytes)))
         return FA_ERR_INVALID_ARG;
+    if (rope) {
+        // tables: [n_pos >= S, D/2] fp32, 16-byte aligned; k_rot (= k here) is
+        // either the input k itself (rotated in place) or clear of every other
+        // buffer, and no output overlaps the tables
+        if (rope->mode != FA_ROPE_HALVES && rope->mode != FA_ROPE_INTERLEAVED)
+            return FA_ERR_INVALID_ARG;
+        if (!rope->k_in || !rope->cos || !rope->sin || rope->n_pos < S)
+            return FA_ERR_INVALID_ARG;
+        const uintptr_t pki = (uintptr_t)rope->k_in, pc = (uintptr_t)rope->cos,
+                        ps = (uintptr_t)rope->sin;
+        if ((pki | pc | ps) & 15u) return FA_ERR_ALIGNMENT;
+        const uint64_t tbytes = (uint64_t)rope->n_pos * (D / 2) * 4;
+        if ((pki != pk && overlaps(pk, nbytes, pki, nbytes)) || overlaps(pk, nbytes, pq, nbytes) ||
+            overlaps(pk, nbytes, pv, nbytes))
+            return FA_ERR_INVALID_ARG;
+        if (overlaps(pk, nbytes, pc, tbytes) || overlaps(pk, nbytes, ps, tbytes) ||
+            overlaps(po, nbytes, pc, tbytes) || overlaps(po, nbytes, ps, tbytes) ||
+            overlaps(po, nbytes, pki, nbytes))
+            return FA_ERR_INVALID_ARG;
+        if (lse && (overlaps(pl, lbytes, pc, tbytes) || overlaps(pl, lbytes, ps, tbytes) ||
+                    overlaps(pl, lbytes, pki, nbytes)))
+            return FA_ERR_INVALID_ARG;
+        if ((uint64_t)bh * S * (D / 16) >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    }
 
     // ---- launch -----------------------------------------------------------
+    if (rope) {
+        fa::RopeParams rp;
+        rp.x = rope->k_in;
+        rp.y = rope->k_rot;
+        rp.cos = rope->cos;
+        rp.sin = rope->sin;
+        rp.rows = (int64_t)bh * S;
+        rp.S = S;
+        rp.interleaved = rope->mode == FA_ROPE_INTERLEAVED;
+        if (fa::launch_rope(rp, D, dtype, stream) != hipSuccess) return FA_ERR_HIP;
+    }
     fa::FwdParams p;
     p.q = q;
     p.k = k;
@@ -186,7 +233,60 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
     p.row_stride = D;
     p.cu_seqlens = nullptr;
     p.total_tokens = 0;
+    p.rope_cos = rope ? rope->cos : nullptr;
+    p.rope_sin = rope ? rope->sin : nullptr;
+    p.rope_interleaved = rope ? rope->mode == FA_ROPE_INTERLEAVED : 0;
     return plan_and_launch_fwd(p, bh, n_qtiles, D, dtype, stream);
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int B, int H, int S, int D, float scale, int mask_mode, int win_l,
+                      int win_r, int dtype, hipStream_t stream) {
+    return fwd_core(q, k, v, o, lse, B, H, S, D, scale, mask_mode, win_l, win_r, dtype, stream,
+                    nullptr);
+}
+
+extern "C" int fa_fwd_rope(const void *q, const void *k, const void *v, void *o, float *lse,
+                           void *k_rot, const float *cos_table, const float *sin_table,
+                           int n_pos, int rope_mode, int B, int H, int S, int D, float scale,
+                           int mask_mode, int win_l, int win_r, int dtype,
+                           hipStream_t stream) {
+    if (!k_rot) return FA_ERR_INVALID_ARG;
+    RopeArgs r{k, k_rot, cos_table, sin_table, n_pos, rope_mode};
+    return fwd_core(q, k_rot, v, o, lse, B, H, S, D, scale, mask_mode, win_l, win_r, dtype,
+                    stream, &r);
+}
+
+extern "C" int fa_rope(const void *x, void *y, const float *cos_table, const float *sin_table,
+                       int n_pos, int rope_mode, int B, int H, int S, int D, int dtype,
+                       hipStream_t stream) {
+    if (B < 0 || H < 0 || S < 0) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (rope_mode != FA_ROPE_HALVES && rope_mode != FA_ROPE_INTERLEAVED) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * S == 0) return FA_OK;
+    if (n_pos < S) return FA_ERR_INVALID_ARG;
+    const uint64_t rows = (uint64_t)B * H * S;
+    if (rows * (D / 16) >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    if (!x || !y || !cos_table || !sin_table) return FA_ERR_INVALID_ARG;
+    const uintptr_t px = (uintptr_t)x, py = (uintptr_t)y, pc = (uintptr_t)cos_table,
+                    ps = (uintptr_t)sin_table;
+    if ((px | py | pc | ps) & 15u) return FA_ERR_ALIGNMENT;
+    const uint64_t nbytes = rows * D * 2, tbytes = (uint64_t)n_pos * (D / 2) * 4;
+    if (px != py && overlaps(px, nbytes, py, nbytes)) return FA_ERR_INVALID_ARG;
+    if (overlaps(py, nbytes, pc, tbytes) || overlaps(py, nbytes, ps, tbytes))
+        return FA_ERR_INVALID_ARG;
+    fa::RopeParams rp;
+    rp.x = x;
+    rp.y = y;
+    rp.cos = cos_table;
+    rp.sin = sin_table;
+    rp.rows = (int64_t)rows;
+    rp.S = S;
+    rp.interleaved = rope_mode == FA_ROPE_INTERLEAVED;
+    return fa::launch_rope(rp, D, dtype, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 extern "C" int fa_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -245,6 +345,8 @@ extern "C" int fa_fwd_varlen(const void *q, const void *k, const void *v, void *
     p.negate_q = scale < 0.0f;
     p.row_stride = H * D;
     p.total_tokens = total_tokens;
+    p.rope_cos = p.rope_sin = nullptr;
+    p.rope_interleaved = 0;
     // At most kMaxPackedSeqs sequences per launch (the kernel's LDS table).
     for (int first = 0; first < nseq; first += fa::kMaxPackedSeqs) {
         const int n = std::min(nseq - first, fa::kMaxPackedSeqs);

@@ -137,6 +137,65 @@ __device__ __forceinline__ float sum_with_partner(float x) {
            __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// ---- rotary position embedding (RoPE) -----------------------------------------
+// Pair (a, b) turned by the angle with cosine c and sine s, in fp32:
+// a' = a c - b s, b' = b c + a s. The D dimensions of a row form D/2 pairs,
+// pair t being dims (t, t + D/2) ("halves") or (2t, 2t + 1) ("interleaved");
+// a row at position p takes c, s from row p of [n_pos, D/2] fp32 tables.
+__device__ __forceinline__ void rotate(float &a, float &b, float c, float s) {
+    const float na = a * c - b * s;
+    const float nb = b * c + a * s;
+    a = na;
+    b = nb;
+}
+
+__device__ __forceinline__ float4 load_f4(const float *p) {
+    return *reinterpret_cast<const float4 *>(p);
+}
+
+// RoPE of one row held as D/16 fragments of 8 values, fragment c holding dims
+// 8 * (2c + g) .. + 7 (the MFMA operand layout of a 32-row block: the lane's
+// half g = 0, 1 holds every other 8-dim chunk). cs and sn point at the row's
+// table rows. Under halves the partner of dim d < D/2 is d + D/2, which lies
+// in fragment c + D/32 of the same lane.
+template <typename T, int D>
+__device__ __forceinline__ void rope_fragments(typename Elem<T>::vec8 (&x)[D / 16], int g,
+                                               const float *cs, const float *sn,
+                                               bool interleaved) {
+    constexpr int NC = D / 16;
+    if (!interleaved) {
+#pragma unroll
+        for (int c = 0; c < NC / 2; ++c) {
+            const int t0 = 8 * (2 * c + g);
+            const float4 c0 = load_f4(cs + t0), c1 = load_f4(cs + t0 + 4);
+            const float4 s0 = load_f4(sn + t0), s1 = load_f4(sn + t0 + 4);
+            const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float a = (float)x[c][e], b = (float)x[c + NC / 2][e];
+                rotate(a, b, cc[e], ss[e]);
+                x[c][e] = (T)a;
+                x[c + NC / 2][e] = (T)b;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int t0 = 4 * (2 * c + g);
+            const float4 c0 = load_f4(cs + t0), s0 = load_f4(sn + t0);
+            const float cc[4] = {c0.x, c0.y, c0.z, c0.w};
+            const float ss[4] = {s0.x, s0.y, s0.z, s0.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float a = (float)x[c][2 * e], b = (float)x[c][2 * e + 1];
+                rotate(a, b, cc[e], ss[e]);
+                x[c][2 * e] = (T)a;
+                x[c][2 * e + 1] = (T)b;
+            }
+        }
+    }
+}
 
 }  // namespace dev
 }  // namespace fa

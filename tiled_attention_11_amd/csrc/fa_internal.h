@@ -46,7 +46,24 @@ struct FwdParams {
     int row_stride;
     const int32_t *cu_seqlens;
     int total_tokens;
+    // Rotary embedding of the query rows (rope_cos == nullptr: none): row i of
+    // a sequence turns by the angles of row i of the [>= S, D/2] fp32 tables,
+    // pairs of halves or (rope_interleaved) of neighbours. k is read as given.
+    const float *rope_cos, *rope_sin;
+    int rope_interleaved;
 };
+
+// Rotary embedding of x [rows / S, S, D] into y (may be x): row r at position r % S.
+struct RopeParams {
+    const void *x;
+    void *y;
+    const float *cos, *sin;  // [>= S, D/2]
+    int64_t rows;
+    int S;
+    int interleaved;
+};
+
+hipError_t launch_rope(const RopeParams &p, int D, int dtype, hipStream_t stream);
 
 // Query rows per workgroup of every kernel variant.
 constexpr int kBlockM = 256;

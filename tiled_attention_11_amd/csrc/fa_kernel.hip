@@ -82,7 +82,8 @@ template <int D> struct Geom {
 
 // PACKED: rows of a head lie H * D elements apart in packed [T, H, D] tensors
 // of variable-length sequences (FwdParams row addressing); otherwise [B, H, S, D].
-template <typename T, int D, bool PACKED>
+// ROPE: query rows get their rotary embedding as they are read (FwdParams).
+template <typename T, int D, bool PACKED, bool ROPE>
 struct Kernel {
     typedef Geom<D> G;
     typedef typename Elem<T>::vec8 vec8;
@@ -737,6 +738,11 @@ struct Kernel {
                     x ^= flip;
                     st.qf[c] = __builtin_bit_cast(vec8, x);
                 }
+                if constexpr (ROPE) {  // rotary embedding of the row at its position
+                    const int64_t at = (int64_t)min(qi, S - 1) * (D / 2);
+                    rope_fragments<T, D>(st.qf, g, p.rope_cos + at, p.rope_sin + at,
+                                         p.rope_interleaved != 0);
+                }
             }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
@@ -785,18 +791,22 @@ struct Kernel {
     }
 };
 
-template <typename T, int D, bool PACKED>
+template <typename T, int D, bool PACKED, bool ROPE>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdParams p) {
+    typedef Kernel<T, D, PACKED, ROPE> K;
     __shared__ __attribute__((aligned(1024)))
-    char smem[Kernel<T, D, PACKED>::kTabOffset + (PACKED ? kMaxPackedSeqs * 8 : 0)];
-    Kernel<T, D, PACKED>::run(p, (LDS char *)smem);
+    char smem[K::kTabOffset + (PACKED ? kMaxPackedSeqs * 8 : 0)];
+    K::run(p, (LDS char *)smem);
 }
 
 template <typename T, int D>
 hipError_t launch_t(const FwdParams &p, hipStream_t stream) {
     void *args[] = {const_cast<FwdParams *>(&p)};
-    const void *fn = p.cu_seqlens ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, true>)
-                                  : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false>);
+    // packed sequences take no rotary embedding
+    const void *fn =
+        p.cu_seqlens ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, true, false>)
+        : p.rope_cos ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, true>)
+                     : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, false>);
     return hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, 0, stream);
 }
 
