@@ -52,6 +52,10 @@ def _bind(lib):
         _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64, _i64,
         ctypes.c_int, _ptr, _ptr, ctypes.c_int, _i64, _ptr, _ptr, _ptr, ctypes.c_int]
     lib.oracle_attention_rope_rows.restype = ctypes.c_int
+    lib.oracle_attention_bwd.argtypes = [
+        _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64,
+        _i64, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
+    lib.oracle_attention_bwd.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [_ptr, _i64, ctypes.c_int, _ptr]
     lib.oracle_decode.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -273,6 +277,23 @@ class Oracle:
             o[a:b] = os_[0].transpose(1, 0, 2)
             lse[a:b] = ls[0].T
         return o, lse
+
+    def attention_bwd(self, q, k, v, dout, dtype, scale, mask, window=(-1, -1), nthreads=0):
+        """Gradients of the attention: ``(dq, dk, dv)`` and the magnitude sums
+        ``(mag_dq, mag_dk, mag_dv)``, float64 [B,H,S,D] each, for uint16 bit
+        inputs q, k, v and dout (= dL/dO) of one [B,H,S,D] shape."""
+        arrs = [np.ascontiguousarray(x, dtype=np.uint16) for x in (q, k, v, dout)]
+        if arrs[0].ndim != 4 or any(a.shape != arrs[0].shape for a in arrs):
+            raise ValueError("q, k, v, dout must share one [B, H, S, D] shape")
+        B, H, S, D = arrs[0].shape
+        m, wl, wr = self._mask_args(mask, window)
+        outs = [np.empty((B, H, S, D), dtype=np.float64) for _ in range(6)]
+        rc = self.lib.oracle_attention_bwd(
+            *(a.ctypes.data for a in arrs), B, H, S, D, float(scale), m, wl, wr, _DTYPES[dtype],
+            *(o.ctypes.data for o in outs), int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_attention_bwd rejected its arguments")
+        return tuple(outs[:3]), tuple(outs[3:])
 
     def max_threads(self):
         return int(self.lib.oracle_max_threads())

@@ -522,6 +522,136 @@ int oracle_attention_rope_rows(const uint16_t *q, const uint16_t *k, const uint1
     return failed ? -1 : 0;
 }
 
+/* Gradients of the attention (the backward pass) for every head of
+ * [B,H,S,D] inputs, given dO = dL/dO for some loss L.
+ * The ops-transformer walkthrough (hwcomputing.csdn.net, 6a0ef689), closing
+ * remark, notes that the backward pass needs state kept from the forward pass
+ * and does not spell it out; what it computes is fixed by the calculus of the
+ * forward's plain definition, written out here per head with P materialised:
+ *   P_ij  = softmax_j(s_ij) as in the forward (0 where hidden),
+ *   dV_j  = sum_i P_ij dO_i,
+ *   dP_ij = dO_i . V_j,
+ *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)        (the softmax Jacobian),
+ *   dQ_i  = scale sum_j dS_ij K_j,    dK_j = scale sum_i dS_ij Q_i.
+ * (sum_k P_ik dP_ik equals dO_i . O_i.) A row with no visible key (not
+ * reachable with these masks) contributes nothing.
+ * Besides the gradients it returns, for the comparison rule of the tests,
+ * the sums of the magnitudes of the terms each gradient element adds up,
+ * with A_i = sum_d |dO_id O_id|:
+ *   mag_dv_jd = sum_i P_ij |dO_id|,
+ *   mag_dq_id = scale sum_j (|dS_ij| + P_ij A_i) |K_jd|,
+ *   mag_dk_jd = scale sum_i (|dS_ij| + P_ij A_i) |Q_id|.
+ * All outputs are fp64 [B,H,S,D]. nthreads <= 0 uses the OpenMP default.
+ * Returns 0, or -1 on a bad argument or allocation failure. */
+int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const uint16_t *dout, int64_t B, int64_t H, int64_t S, int64_t D,
+                         double scale, int mask_mode, int64_t wl, int64_t wr, int dtype,
+                         double *dq, double *dk, double *dv, double *mag_dq, double *mag_dk,
+                         double *mag_dv, int nthreads)
+{
+    if (check_args(B, H, S, D, mask_mode, dtype)) return -1;
+    if (S == 0) return 0;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    const size_t hd = (size_t)(S * D), ss = (size_t)(S * S);
+    double *qd = (double *)malloc(sizeof(double) * hd), *kd = (double *)malloc(sizeof(double) * hd);
+    double *vd = (double *)malloc(sizeof(double) * hd), *dod = (double *)malloc(sizeof(double) * hd);
+    double *P = (double *)malloc(sizeof(double) * ss), *dS = (double *)malloc(sizeof(double) * ss);
+    double *A = (double *)malloc(sizeof(double) * (size_t)S);
+    int failed = !qd || !kd || !vd || !dod || !P || !dS || !A;
+    for (int64_t bh = 0; bh < B * H && !failed; ++bh) {
+        const int64_t base = bh * S * D;
+        for (size_t t = 0; t < hd; ++t) {
+            qd[t] = decode(q[base + t], dtype);
+            kd[t] = decode(k[base + t], dtype);
+            vd[t] = decode(v[base + t], dtype);
+            dod[t] = decode(dout[base + t], dtype);
+        }
+        /* rows: probabilities, dS, dQ */
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 4)
+        for (int64_t i = 0; i < S; ++i) {
+            double *Pi = P + i * S, *dSi = dS + i * S;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < S; ++j) {
+                if (!oracle_visible(i, j, mask_mode, wl, wr)) {
+                    Pi[j] = -INFINITY;
+                    continue;
+                }
+                double acc = 0.0;
+                for (int64_t d = 0; d < D; ++d) acc += qd[i * D + d] * kd[j * D + d];
+                Pi[j] = scaled(acc, scale);
+                if (Pi[j] > m) m = Pi[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < S; ++j) {
+                Pi[j] = (m == -INFINITY || Pi[j] == -INFINITY) ? 0.0 : exp(Pi[j] - m);
+                l += Pi[j];
+            }
+            for (int64_t j = 0; j < S; ++j) Pi[j] = l > 0.0 ? Pi[j] / l : 0.0;
+            /* dP, its P-weighted row sum, dS; A_i from O_i = sum_j P_ij V_j */
+            double dsum = 0.0, a = 0.0;
+            for (int64_t j = 0; j < S; ++j) {
+                double dp = 0.0;
+                if (Pi[j] != 0.0)
+                    for (int64_t d = 0; d < D; ++d) dp += dod[i * D + d] * vd[j * D + d];
+                dSi[j] = dp;
+                dsum += Pi[j] * dp;
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                double o = 0.0;
+                for (int64_t j = 0; j < S; ++j) o += Pi[j] * vd[j * D + d];
+                a += fabs(dod[i * D + d] * o);
+            }
+            A[i] = a;
+#if ORACLE_PLANT == 10
+            (void)dsum;
+            for (int64_t j = 0; j < S; ++j) dSi[j] = Pi[j] * dSi[j];  /* planted: no row term */
+#else
+            for (int64_t j = 0; j < S; ++j) dSi[j] = Pi[j] * (dSi[j] - dsum);
+#endif
+            for (int64_t d = 0; d < D; ++d) {
+                double g = 0.0, mg = 0.0;
+                for (int64_t j = 0; j < S; ++j) {
+                    g += dSi[j] * kd[j * D + d];
+                    mg += (fabs(dSi[j]) + Pi[j] * a) * fabs(kd[j * D + d]);
+                }
+                dq[base + i * D + d] = scale * g;
+                mag_dq[base + i * D + d] = fabs(scale) * mg;
+            }
+        }
+        /* columns: dK, dV */
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 4)
+        for (int64_t j = 0; j < S; ++j) {
+            for (int64_t d = 0; d < D; ++d) {
+                double gk = 0.0, gv = 0.0, mk = 0.0, mv = 0.0;
+                for (int64_t i = 0; i < S; ++i) {
+                    const double p = P[i * S + j], ds = dS[i * S + j];
+                    if (p == 0.0 && ds == 0.0) continue;
+                    gv += p * dod[i * D + d];
+                    mv += p * fabs(dod[i * D + d]);
+                    gk += ds * qd[i * D + d];
+                    mk += (fabs(ds) + p * A[i]) * fabs(qd[i * D + d]);
+                }
+                dv[base + j * D + d] = gv;
+                mag_dv[base + j * D + d] = mv;
+                dk[base + j * D + d] = scale * gk;
+                mag_dk[base + j * D + d] = fabs(scale) * mk;
+            }
+        }
+    }
+    free(qd);
+    free(kd);
+    free(vd);
+    free(dod);
+    free(P);
+    free(dS);
+    free(A);
+    return failed ? -1 : 0;
+}
+
 /* Decode n raw 16-bit values to fp64 with the oracle's own decoders. */
 void oracle_decode(const uint16_t *x, int64_t n, int dtype, double *out)
 {

@@ -516,6 +516,57 @@ def pin_rope_zero_angle_is_plain_attention(orc):
         assert np.array_equal(o, o0) and np.array_equal(lse, lse0)
 
 
+def pin_bwd_autograd(orc):
+    """The gradients equal torch autograd through fp64 scaled_dot_product_attention
+    (CPU) with the mask; every magnitude sum bounds its gradient."""
+    rng = np.random.default_rng(37)
+    for dtype in ("f16", "bf16"):
+        for S in (1, 9, 37):
+            q, k, v = make_qkv(2, 2, S, 16, dtype, seed=int(rng.integers(1 << 30)))
+            do, _, _ = make_qkv(2, 2, S, 16, dtype, seed=int(rng.integers(1 << 30)))
+            for mask, window in MASK_CASES:
+                bm = torch.from_numpy(_bool_mask_kv(S, S, mask, window))
+                t = [torch.from_numpy(_decode_ref(x, dtype)).requires_grad_(True)
+                     for x in (q, k, v)]
+                o = torch.nn.functional.scaled_dot_product_attention(*t, attn_mask=bm,
+                                                                     scale=0.45)
+                o.backward(torch.from_numpy(_decode_ref(do, dtype)))
+                (dq, dk, dv), mags = orc.attention_bwd(q, k, v, do, dtype, 0.45, mask, window)
+                for got, ref in zip((dq, dk, dv), t):
+                    assert np.max(np.abs(got - ref.grad.numpy())) < 1e-11, (dtype, S, mask, window)
+                for g, m in zip((dq, dk, dv), mags):
+                    assert np.all(np.abs(g) <= m * (1 + 1e-12) + 1e-300)
+
+
+def pin_bwd_closed_forms(orc):
+    """Q = 0 (uniform weights): dV_j is the sum over the rows that see key j of
+    dO_i divided by their visible-key count, and dK = 0 when V rows are all
+    equal (dP is constant along each row, so dS = 0); constant K rows give
+    dQ = 0 (each row of dS sums to zero); and sum(dQ * Q) = sum(dK * K)."""
+    S, D = 23, 8
+    _, k, v = make_qkv(1, 2, S, D, "f16", seed=38)
+    do, _, _ = make_qkv(1, 2, S, D, "f16", seed=39)
+    q0 = np.zeros_like(k)
+    dod = _decode_ref(do, "f16")
+    for mask, window in MASK_CASES:
+        vis = _bool_mask_kv(S, S, mask, window)
+        (dq, dk, dv), _ = orc.attention_bwd(q0, k, v, do, "f16", 0.7, mask, window)
+        w = vis / vis.sum(axis=1, keepdims=True)          # uniform weights per row
+        ref = np.einsum("ij,bhid->bhjd", w, dod)
+        assert np.max(np.abs(dv - ref)) < 1e-12, (mask, window)
+    vconst = np.broadcast_to(v[:, :, :1, :], v.shape).copy()
+    (dq, dk, dv), _ = orc.attention_bwd(k, k, vconst, do, "f16", 0.7, "causal")
+    assert np.max(np.abs(dk)) < 1e-12 and np.max(np.abs(dq)) < 1e-12
+    kconst = np.broadcast_to(k[:, :, :1, :], k.shape).copy()
+    q, _, _ = make_qkv(1, 2, S, D, "f16", seed=40)
+    (dq, dk, dv), _ = orc.attention_bwd(q, kconst, v, do, "f16", 0.7, "full")
+    assert np.max(np.abs(dq)) < 1e-12
+    (dq, dk, dv), _ = orc.attention_bwd(q, k, v, do, "f16", 0.7, "window", (5, 2))
+    lhs = np.sum(dq * _decode_ref(q, "f16"))
+    rhs = np.sum(dk * _decode_ref(k, "f16"))
+    assert abs(lhs - rhs) < 1e-10 * (1 + abs(lhs))
+
+
 def pin_kv_is_the_tail_of_the_square_case(orc):
     """New rows at the end of a sequence give the last rows of the square
     problem whose query rows end with them (any earlier query rows)."""
@@ -570,4 +621,6 @@ ALL_PINS = [
     pin_rope_is_complex_rotation,
     pin_rope_attention_sdpa,
     pin_rope_zero_angle_is_plain_attention,
+    pin_bwd_autograd,
+    pin_bwd_closed_forms,
 ]

@@ -5,7 +5,8 @@ Planted mistakes (see ORACLE_PLANT in oracle/attn_oracle.c):
   1 scale dropped, 2 causal diagonal dropped, 3 window left edge exclusive,
   4 score sign flipped, 5 wrong V row, 6 log base 2 in the LSE,
   7 cache rows aligned top-left instead of at the end of the sequence,
-  8 RoPE rotation turned the wrong way, 9 rounding ties away from zero.
+  8 RoPE rotation turned the wrong way, 9 rounding ties away from zero,
+  10 backward without the softmax Jacobian's row term.
 """
 import os
 
@@ -15,7 +16,7 @@ import oracle
 from oracle_pins import ALL_PINS
 
 
-@pytest.mark.parametrize("plant", [1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("plant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_planted_mistake_is_caught(plant):
     bad = oracle.load_planted(plant)
     try:
