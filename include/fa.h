@@ -172,6 +172,47 @@ int64_t fa_fwd_varlen_flops(const int32_t *cu_seqlens, int nseq, int H, int D,
                             int mask_mode, int win_l, int win_r);
 
 /*
+ * fa_bwd -- the attention backward pass: the gradients dQ, dK, dV of
+ * O = softmax(scale * Q K^T + mask) V for a given dO = dL/dO, from the
+ * forward's O and LSE (the state the forward keeps):
+ *     P_ij = exp(scale q_i . k_j - LSE_i) on visible pairs, 0 elsewhere,
+ *     D_i = dO_i . O_i,   dS_ij = P_ij (dO_i . v_j - D_i),
+ *     dV_j = sum_i P_ij dO_i,  dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+ * Defining passage: ops-transformer FlashAttention walkthrough
+ * (hwcomputing.csdn.net, 6a0ef689), closing remark (the backward needs the
+ * forward's intermediate state), read as the gradient of fa_fwd's definition
+ * recomputing P from the saved LSE.
+ *
+ * q, k, v, o, dout  device pointers, contiguous [B, H, S, D] of `dtype`, 16-byte
+ *             aligned; o and lse as fa_fwd returned them for q, k, v and the same
+ *             scale and mask; read only.
+ * lse         device pointer to fp32 [B, H, S] (natural log); read only.
+ * dq, dk, dv  device pointers, [B, H, S, D] of `dtype`, 16-byte aligned; fully
+ *             overwritten (fp32 accumulation, rounded RNE once).
+ * workspace   device memory of at least fa_bwd_workspace_bytes(B, H, S) bytes,
+ *             4-byte aligned (it receives D_i); contents on entry do not matter.
+ * B, H, S, D, scale, mask_mode, win_l, win_r, dtype, stream: as for fa_fwd.
+ * Outputs and workspace must not overlap any input or each other (checked).
+ * Arithmetic: S, dP, dV, dK, dQ on fp16/bf16 matrix cores with fp32
+ * accumulation; P and dS are formed in fp32 and rounded to `dtype` as MFMA
+ * operands. Deterministic: every output element is owned by one workgroup
+ * (no atomics). Returns FA_OK or a negative fa_status.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, int B, int H, int S, int D,
+           float scale, int mask_mode, int win_l, int win_r, int dtype, void *workspace,
+           int64_t workspace_bytes, hipStream_t stream);
+
+/* fa_bwd_workspace_bytes -- workspace fa_bwd needs: 4 * B * H * S bytes (or a
+ * negative fa_status). */
+int64_t fa_bwd_workspace_bytes(int B, int H, int S);
+
+/* fa_bwd_flops -- algorithmic FLOPs of one fa_bwd call: the five products over
+ * the visible pairs, 10 * D * B * H * fa_visible_pairs(S, ...) (2.5 times
+ * fa_fwd_flops). Returns the count, or a negative fa_status. */
+int64_t fa_bwd_flops(int B, int H, int S, int D, int mask_mode, int win_l, int win_r);
+
+/*
  * fa_rope -- rotary position embedding (RoPE) of a [B, H, S, D] tensor: pair
  * t of row s of every head (see fa_rope_mode) turns by the angle whose cosine
  * and sine are cos_table[s * D/2 + t] and sin_table[s * D/2 + t]:

@@ -537,10 +537,14 @@ int oracle_attention_rope_rows(const uint16_t *q, const uint16_t *k, const uint1
  * reachable with these masks) contributes nothing.
  * Besides the gradients it returns, for the comparison rule of the tests,
  * the sums of the magnitudes of the terms each gradient element adds up,
- * with A_i = sum_d |dO_id O_id|:
- *   mag_dv_jd = sum_i P_ij |dO_id|,
- *   mag_dq_id = scale sum_j (|dS_ij| + P_ij A_i) |K_jd|,
- *   mag_dk_jd = scale sum_i (|dS_ij| + P_ij A_i) |Q_id|.
+ * with A_i = sum_d |dO_id O_id| and, for a visible pair, |x|_t = max(|x|, t)
+ * where t is the element type's smallest normal (2^-14 for binary16, 2^-126
+ * for bfloat16: below it, rounding to the type errs by up to half the
+ * subnormal spacing, t times the unit roundoff, rather than by a relative
+ * amount):
+ *   mag_dv_jd = sum_i |P_ij|_t |dO_id|,
+ *   mag_dq_id = |scale| sum_j (|dS_ij|_t + P_ij A_i) |K_jd|,
+ *   mag_dk_jd = |scale| sum_i (|dS_ij|_t + P_ij A_i) |Q_id|.
  * All outputs are fp64 [B,H,S,D]. nthreads <= 0 uses the OpenMP default.
  * Returns 0, or -1 on a bad argument or allocation failure. */
 int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -562,6 +566,7 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
     double *P = (double *)malloc(sizeof(double) * ss), *dS = (double *)malloc(sizeof(double) * ss);
     double *A = (double *)malloc(sizeof(double) * (size_t)S);
     int failed = !qd || !kd || !vd || !dod || !P || !dS || !A;
+    const double tiny = dtype == ORACLE_BF16 ? ldexp(1.0, -126) : ldexp(1.0, -14);
     for (int64_t bh = 0; bh < B * H && !failed; ++bh) {
         const int64_t base = bh * S * D;
         for (size_t t = 0; t < hd; ++t) {
@@ -615,8 +620,9 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
             for (int64_t d = 0; d < D; ++d) {
                 double g = 0.0, mg = 0.0;
                 for (int64_t j = 0; j < S; ++j) {
+                    if (Pi[j] == 0.0) continue;          /* hidden (or underflowed) pair */
                     g += dSi[j] * kd[j * D + d];
-                    mg += (fabs(dSi[j]) + Pi[j] * a) * fabs(kd[j * D + d]);
+                    mg += (fmax(fabs(dSi[j]), tiny) + Pi[j] * a) * fabs(kd[j * D + d]);
                 }
                 dq[base + i * D + d] = scale * g;
                 mag_dq[base + i * D + d] = fabs(scale) * mg;
@@ -629,11 +635,11 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
                 double gk = 0.0, gv = 0.0, mk = 0.0, mv = 0.0;
                 for (int64_t i = 0; i < S; ++i) {
                     const double p = P[i * S + j], ds = dS[i * S + j];
-                    if (p == 0.0 && ds == 0.0) continue;
+                    if (p == 0.0) continue;              /* hidden (or underflowed) pair */
                     gv += p * dod[i * D + d];
-                    mv += p * fabs(dod[i * D + d]);
+                    mv += fmax(p, tiny) * fabs(dod[i * D + d]);
                     gk += ds * qd[i * D + d];
-                    mk += (fabs(ds) + p * A[i]) * fabs(qd[i * D + d]);
+                    mk += (fmax(fabs(ds), tiny) + p * A[i]) * fabs(qd[i * D + d]);
                 }
                 dv[base + j * D + d] = gv;
                 mag_dv[base + j * D + d] = mv;

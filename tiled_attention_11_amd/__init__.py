@@ -2,11 +2,12 @@
 
 A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
 ``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops``, ``fa_fwd_varlen``,
-``fa_fwd_varlen_flops``, ``fa_rope``, ``fa_fwd_rope``, ``fa_decode``,
+``fa_fwd_varlen_flops``, ``fa_rope``, ``fa_fwd_rope``, ``fa_bwd``,
+``fa_bwd_workspace_bytes``, ``fa_bwd_flops``, ``fa_decode``,
 ``fa_decode_workspace_bytes``, ``fa_decode_flops``, ``fa_decode_paged``,
 ``fa_decode_paged_workspace_bytes`` and ``fa_strerror`` carry the C names and
 arguments (marshalling only). ``forward``, ``forward_varlen``, ``rope``,
-``forward_rope``, ``decode`` and ``decode_paged`` are the convenience entries
+``forward_rope``, ``backward``, ``decode`` and ``decode_paged`` are the convenience entries
 for torch tensors: torch supplies device memory and the stream; every step of
 the computation runs in the library's HIP kernels.
 There is no fallback: if the library is missing, importing this package
@@ -20,8 +21,8 @@ __all__ = [
     "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
     "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
     "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_rope", "fa_fwd_rope", "FA_ROPE_HALVES",
-    "FA_ROPE_INTERLEAVED", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
-    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "forward_varlen", "rope", "forward_rope", "decode",
+    "FA_ROPE_INTERLEAVED", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_flops", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
+    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "forward_varlen", "rope", "forward_rope", "backward", "decode",
     "decode_paged",
     "lib_path", "library",
 ]
@@ -72,6 +73,13 @@ def _load():
     lib.fa_fwd_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                 ctypes.c_float, ci, ci, ci, ci, vp]
     lib.fa_fwd_rope.restype = ci
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ctypes.c_float,
+                           ci, ci, ci, ci, vp, i64, vp]
+    lib.fa_bwd.restype = ci
+    lib.fa_bwd_workspace_bytes.argtypes = [ci, ci, ci]
+    lib.fa_bwd_workspace_bytes.restype = i64
+    lib.fa_bwd_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci]
+    lib.fa_bwd_flops.restype = i64
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci,
                               ci, ci, vp, i64, vp]
     lib.fa_decode.restype = ci
@@ -145,6 +153,21 @@ def fa_fwd_rope(q, k, v, o, lse, k_rot, cos_table, sin_table, n_pos, rope_mode, 
     """Call ``fa_fwd_rope`` with raw device addresses (ints); return its status."""
     return _lib.fa_fwd_rope(q, k, v, o, lse, k_rot, cos_table, sin_table, n_pos, rope_mode, B,
                             H, S, D, scale, mask_mode, win_l, win_r, dtype, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, S, D, scale, mask_mode, win_l, win_r,
+           dtype, workspace, workspace_bytes, stream):
+    """Call ``fa_bwd`` with raw device addresses (ints); return its status."""
+    return _lib.fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, S, D, scale, mask_mode, win_l,
+                       win_r, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, S):
+    return _lib.fa_bwd_workspace_bytes(B, H, S)
+
+
+def fa_bwd_flops(B, H, S, D, mask_mode, win_l=-1, win_r=-1):
+    return _lib.fa_bwd_flops(B, H, S, D, mask_mode, win_l, win_r)
 
 
 def fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
@@ -381,6 +404,57 @@ def forward_rope(q, k, v, cos, sin, *, mode="halves", k_rot=None, scale=None, ma
     if status != 0:
         raise FaError(status, "fa_fwd_rope")
     return out, lse, k_rot
+
+
+def backward(q, k, v, o, lse, dout, *, scale=None, mask="full", window=(-1, -1), dq=None,
+             dk=None, dv=None, workspace=None, stream=None):
+    """Gradients ``(dq, dk, dv)`` of the attention for ``dout`` = dL/dO, given the
+    forward's ``o`` and ``lse`` (from ``forward`` with the same q, k, v, scale
+    and mask). All of q, k, v, o, dout contiguous [B, H, S, D] of one dtype;
+    lse float32 [B, H, S]. ``workspace``: optional uint8 device tensor of at
+    least ``fa_bwd_workspace_bytes(B, H, S)`` bytes (allocated when not given)."""
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, dout must share one [B, H, S, D] shape")
+    if not q.is_cuda or any(t.device != q.device for t in ts):
+        raise ValueError("q, k, v, o, dout must be on the same GPU")
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in ts):
+        raise ValueError("q, k, v, o, dout must all be float16 or all bfloat16")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("q, k, v, o, dout must be contiguous")
+    B, H, S, D = q.shape
+    if (lse.shape != (B, H, S) or lse.dtype != torch.float32 or lse.device != q.device
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    grads = []
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if g is None:
+            g = torch.empty_like(q)
+        elif g.shape != q.shape or g.dtype != q.dtype or g.device != q.device or not g.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+        grads.append(g)
+    need = fa_bwd_workspace_bytes(B, H, S)
+    if need < 0:
+        raise FaError(int(need), "fa_bwd")
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 4), dtype=torch.uint8, device=q.device)
+    wl, wr = window
+    dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        status = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                        grads[2].data_ptr(), B, H, S, D, float(scale), _mask_code(mask),
+                        int(wl), int(wr), dtype, workspace.data_ptr(),
+                        workspace.numel() * workspace.element_size(), stream)
+    if status != 0:
+        raise FaError(status, "fa_bwd")
+    return tuple(grads)
 
 
 def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse=None,

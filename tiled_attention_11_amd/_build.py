@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_kernel.hip"),
-           os.path.join(CSRC, "fa_decode.hip"), os.path.join(CSRC, "fa_rope.hip")]
+           os.path.join(CSRC, "fa_decode.hip"), os.path.join(CSRC, "fa_rope.hip"),
+           os.path.join(CSRC, "fa_bwd.hip")]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -373,6 +373,91 @@ extern "C" int64_t fa_fwd_varlen_flops(const int32_t *cu_seqlens, int nseq, int 
     return (int64_t)f;
 }
 
+// ---- backward ---------------------------------------------------------------------
+
+extern "C" int64_t fa_bwd_workspace_bytes(int B, int H, int S) {
+    if (B < 0 || H < 0 || S < 0) return FA_ERR_INVALID_ARG;
+    const __int128 n = (__int128)B * H * S * 4;
+    if (n > (__int128)INT64_MAX) return FA_ERR_TOO_LARGE;
+    return (int64_t)n;
+}
+
+extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                      int H, int S, int D, float scale, int mask_mode, int win_l, int win_r,
+                      int dtype, void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+    // ---- scalar arguments -------------------------------------------------
+    if (B < 0 || H < 0 || S < 0) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    int win_lo, win_hi;
+    if (!window_of(mask_mode, win_l, win_r, &win_lo, &win_hi)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * S == 0) return FA_OK;
+
+    // ---- sizes ------------------------------------------------------------
+    const uint64_t head_bytes = (uint64_t)S * D * 2;
+    if (head_bytes >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    const uint64_t bh = (uint64_t)B * H;
+    const uint64_t tiles = bh * (((uint64_t)S + 127) / 128);
+    if (tiles > (uint64_t)INT32_MAX) return FA_ERR_TOO_LARGE;
+    if (bh * S * (D / 8) >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    const uint64_t nbytes = bh * head_bytes;
+    const uint64_t lbytes = bh * (uint64_t)S * 4;
+    if (nbytes > (uint64_t)INT64_MAX / 4) return FA_ERR_TOO_LARGE;
+
+    // ---- pointers ---------------------------------------------------------
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+        return FA_ERR_INVALID_ARG;
+    if (workspace_bytes < (int64_t)lbytes) return FA_ERR_INVALID_ARG;
+    const uintptr_t in[6] = {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o,
+                             (uintptr_t)dout, (uintptr_t)lse};
+    const uint64_t in_n[6] = {nbytes, nbytes, nbytes, nbytes, nbytes, lbytes};
+    const uintptr_t out[4] = {(uintptr_t)dq, (uintptr_t)dk, (uintptr_t)dv, (uintptr_t)workspace};
+    const uint64_t out_n[4] = {nbytes, nbytes, nbytes, lbytes};
+    for (int t = 0; t < 5; ++t)
+        if (in[t] & 15u) return FA_ERR_ALIGNMENT;
+    for (int t = 0; t < 3; ++t)
+        if (out[t] & 15u) return FA_ERR_ALIGNMENT;
+    if ((in[5] | out[3]) & 3u) return FA_ERR_ALIGNMENT;
+    for (int a = 0; a < 4; ++a) {
+        for (int t = 0; t < 6; ++t)
+            if (overlaps(out[a], out_n[a], in[t], in_n[t])) return FA_ERR_INVALID_ARG;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(out[a], out_n[a], out[b], out_n[b])) return FA_ERR_INVALID_ARG;
+    }
+
+    // ---- launch -----------------------------------------------------------
+    fa::BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = dout;
+    p.lse = lse;
+    p.rowdot = static_cast<float *>(workspace);
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.B = B;
+    p.H = H;
+    p.S = S;
+    p.win_lo = win_lo;
+    p.win_hi = win_hi;
+    p.scale = scale;
+    return fa::launch_bwd(p, D, dtype, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int64_t fa_bwd_flops(int B, int H, int S, int D, int mask_mode, int win_l,
+                                int win_r) {
+    // five products over the visible pairs (S, dP, dV, dK, dQ), 2 FLOPs per
+    // multiply-add each: 10 * D per pair, 2.5 times the forward's count
+    const int64_t f = fa_fwd_flops(B, H, S, D, mask_mode, win_l, win_r);
+    if (f < 0) return f;
+    if (f > INT64_MAX / 10 * 4) return FA_ERR_TOO_LARGE;
+    return f / 4 * 10;
+}
+
 // ---- new query rows against a key/value cache ---------------------------------
 
 namespace {

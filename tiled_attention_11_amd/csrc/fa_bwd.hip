@@ -1,0 +1,454 @@
+// fa_bwd.hip -- the attention backward pass for gfx950 (MI355X): gradients
+// dQ, dK, dV of O = softmax(scale * Q K^T + mask) V for fp16/bf16 [B, H, S, D]
+// tensors, D in {64, 128}, with the forward's LSE as the saved state.
+//
+// What it computes: with P_ij = exp(scale * q_i . k_j - LSE_i) on visible
+// pairs (0 elsewhere) and D_i = dO_i . O_i,
+//   dV_j = sum_i P_ij dO_i,   dS_ij = P_ij (dO_i . V_j - D_i),
+//   dQ_i = scale sum_j dS_ij K_j,   dK_j = scale sum_i dS_ij Q_i:
+// the gradients of the forward's definition (D_i is the softmax Jacobian's
+// row term sum_k P_ik dP_ik). The ops-transformer FlashAttention walkthrough
+// (hwcomputing.csdn.net, 6a0ef689), closing remark, notes that the backward
+// needs state kept from the forward; the LSE is that state, so P is
+// recomputed tile by tile and, as in the forward, no S x S matrix reaches
+// memory.
+//
+// gfx950 design: three kernels.
+//  * fa_bwd_rowdot: D_i = dO_i . O_i (fp32) into the caller's workspace.
+//  * fa_bwd_dq: a workgroup of 4 waves owns 128 query rows (32 per wave, a
+//    row per lane as in the forward) and streams the visible 64-key tiles of
+//    K and V through LDS (direct HBM -> LDS DMA, two stages). Per 32-key
+//    block: S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16 (Q^T, dO^T
+//    fragments held in registers), then P^T, dS^T in fp32 in the accumulator
+//    layout (one query per lane: its LSE and D_i are scalars), and
+//    dQ^T += K^T dS^T with K^T from transposing LDS reads
+//    (ds_read_b64_tr_b16) and dS^T straight from the accumulator.
+//  * fa_bwd_dkdv: the mirror image: a workgroup owns 128 keys (K^T, V^T
+//    fragments in registers, a key per lane) and streams the 64-query tiles
+//    of Q and dO that see them, with their LSE and D_i staged in LDS. Per
+//    32-query block: S = Q K^T and dP = dO V^T, then P and dS (a query per
+//    accumulator row), dV^T += dO^T P and dK^T += Q^T dS.
+//  Each streamed tile is read both row-wise (MFMA A operand) and transposed
+//  (the A operand of the accumulating product), so it is stored twice, once
+//  per LDS swizzle, which keeps both read patterns free of bank conflicts.
+//  dQ and dK/dV each own their outputs, so there are no atomics and the
+//  results are deterministic.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+using namespace dev;
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;  // fixed rows (queries or keys) per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D> struct BGeom {
+    static constexpr int BN = 64;                  // streamed rows per tile
+    static constexpr int RB = 2 * D;               // bytes per row
+    static constexpr int CPR = RB / 16;            // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BN * RB;     // 16 KiB (D = 128), 8 KiB (D = 64)
+    static constexpr int ROWS_PER_KB = 1024 / RB;  // rows per 1 KiB DMA block
+    static constexpr int NBLK = TILE_BYTES / 1024; // DMA blocks per tile
+    static_assert(NBLK % kBwdWaves == 0, "DMA split");
+};
+
+// Swizzles of a tile: row-read (MFMA A operand of rows) or transposed-read.
+enum { kRowSwz = 0, kTrSwz = 1 };
+
+template <typename T, int D>
+struct Bwd {
+    typedef BGeom<D> G;
+    typedef typename Elem<T>::vec8 vec8;
+    static constexpr int BN = G::BN;
+    static constexpr int NDC = D / 16;   // 16-dim chunks of a dims contraction
+    static constexpr int NDB = D / 32;   // 32-dim output blocks
+    static constexpr int NSB = BN / 32;  // 32-row blocks of a streamed tile
+
+    // Stream rows r0 .. r0 + BN - 1 of the [S, D] head at h into the LDS tile
+    // at byte address slot, with the given swizzle (this wave's share of the
+    // 1 KiB DMA blocks). Rows past S read as zero.
+    template <int SW>
+    static __device__ __forceinline__ void load_tile(const uint16_t *h, int r0, int S,
+                                                     uint32_t slot, int wave, int lane) {
+        const i32x4 rsrc =
+            buffer_rsrc(h + (int64_t)r0 * D, r0 < S ? (uint32_t)(S - r0) * G::RB : 0u);
+        const int pc = lane % G::CPR;
+#pragma unroll
+        for (int i = 0; i < G::NBLK / kBwdWaves; ++i) {
+            const int b = i * kBwdWaves + wave;
+            const int row = b * G::ROWS_PER_KB + lane / G::CPR;
+            const int lc = SW == kRowSwz ? kchunk<D>(pc, row) : vchunk<D>(pc, row);
+            dma16(rsrc, slot + (uint32_t)b * 1024u, (uint32_t)(row * G::RB + lc * 16));
+        }
+    }
+
+    // MFMA B-operand fragments of one row (registers): fragment c holds dims
+    // 16c + 8g .. + 7 of row r of the [S, D] head at h; zero past S.
+    static __device__ __forceinline__ void load_frags(const uint16_t *h, int r, int S, int g,
+                                                      vec8 (&f)[NDC]) {
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (r < S) x = *reinterpret_cast<const u32x4 *>(h + (int64_t)r * D + 16 * c + 8 * g);
+            f[c] = __builtin_bit_cast(vec8, x);
+        }
+    }
+
+    // Per-lane LDS offsets. Row read (A operand of 32 rows x 16 dims): row l32,
+    // logical chunk 2c + g. Transposed read (A operand of 32 dims x 16 rows,
+    // dims block db): as the forward's V^T read.
+    struct Offs {
+        uint32_t row[NDC];
+        uint32_t tr[NDB];
+    };
+    static __device__ __forceinline__ void make_offs(Offs &o, int lane) {
+        const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) o.row[c] = l32 * G::RB + kchunk<D>(2 * c + g, l32) * 16;
+        const int q = lane & 15, h = (lane >> 4) & 1;
+        const int trow = 4 * g + (q >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = 32 * db + 16 * h + 4 * (q & 3);
+            o.tr[db] = trow * G::RB + vchunk<D>(col >> 3, trow) * 16 + (col & 7) * 2;
+        }
+    }
+
+    // A operand of 32 rows (block sb of the tile) x dims chunk c.
+    static __device__ __forceinline__ vec8 read_rows(const LDS char *tile, const Offs &o, int sb,
+                                                     int c) {
+        return *reinterpret_cast<const LDS vec8 *>(tile + o.row[c] + sb * 32 * G::RB);
+    }
+    // A operand of 32 dims (block db) x 16 rows (chunk c16 of the tile), from
+    // a tile stored with the transposed-read swizzle. Elements 0-3 are rows
+    // 16 c16 + 4g + 0..3, elements 4-7 the same + 8: the rows an accumulator's
+    // elements 8hh .. 8hh + 7 hold for the chunk's half hh.
+    static __device__ __forceinline__ vec8 read_tr(const LDS char *tile, const Offs &o, int db,
+                                                   int c16) {
+        const LDS char *base = tile + o.tr[db] + 16 * c16 * G::RB;
+        const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base));
+        const fp16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base + 8 * G::RB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(vec8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+    }
+    static __device__ __forceinline__ vec8 half_of(const uint32_t (&pk)[8], int hh) {
+        return __builtin_bit_cast(
+            vec8, u32x4{pk[4 * hh + 0], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]});
+    }
+
+    // Store a D^T accumulator (lane = row r of the output, accumulator rows =
+    // dims) times mul into row r of the [S, D] head at out.
+    static __device__ __forceinline__ void store_rows(uint16_t *out, int r, int g,
+                                                      const f32x16 (&acc)[NDB], float mul) {
+        uint16_t *orow = out + (int64_t)r * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                u32x2 w;
+                w[0] = Elem<T>::pack(acc[db][4 * a + 0] * mul, acc[db][4 * a + 1] * mul);
+                w[1] = Elem<T>::pack(acc[db][4 * a + 2] * mul, acc[db][4 * a + 3] * mul);
+                *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * a + 4 * g) = w;
+            }
+    }
+
+    // ---- dQ -------------------------------------------------------------------
+    // LDS per stage: K rows (row swizzle), K (transposed swizzle), V rows.
+    static constexpr uint32_t kDqStage = 3 * G::TILE_BYTES;
+
+    static __device__ void dq(const BwdParams &p, LDS char *smem) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int l32 = lane & 31, g = lane >> 5;
+        const int S = p.S;
+        const int ntq = (S + kBwdRows - 1) / kBwdRows;
+        const int bh = (int)blockIdx.x / ntq;
+        const int qt = ntq - 1 - ((int)blockIdx.x - bh * ntq);  // longest rows first
+        const int q0 = qt * kBwdRows, qi = q0 + 32 * wave + l32;
+        const int64_t head = (int64_t)bh * S * D;
+        const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
+        const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
+        const uint16_t *vh = static_cast<const uint16_t *>(p.v) + head;
+        const uint16_t *doh = static_cast<const uint16_t *>(p.dout) + head;
+
+        vec8 qf[NDC], df[NDC];
+        load_frags(qh, qi, S, g, qf);
+        load_frags(doh, qi, S, g, df);
+        const float lse2 = qi < S ? p.lse[(int64_t)bh * S + qi] * kLog2e : 0.0f;
+        const float drow = qi < S ? p.rowdot[(int64_t)bh * S + qi] : 0.0f;
+        const float c2 = p.scale * kLog2e;
+
+        const int qlast = min(q0 + kBwdRows - 1, S - 1);
+        const int t_first = max(0, q0 - p.win_lo) / BN;
+        const int t_last = min(S - 1, qlast + p.win_hi) / BN;
+        // tiles visible in full from every row of the workgroup
+        const int t_in_lo = (max(0, qlast - p.win_lo) + BN - 1) / BN;
+        const int t_in_hi = (min(S - 1, q0 + p.win_hi) + 1) / BN;
+
+        Offs o;
+        make_offs(o, lane);
+        const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+        auto issue = [&](int t, int s) {
+            const uint32_t st = sbase + s * kDqStage;
+            load_tile<kRowSwz>(kh, t * BN, S, st, wave, lane);
+            load_tile<kTrSwz>(kh, t * BN, S, st + G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz>(vh, t * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
+        };
+
+        f32x16 acc[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+        issue(t_first, 0);
+        for (int t = t_first; t <= t_last; ++t) {
+            const int s = (t - t_first) & 1;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // tile t is in LDS; every wave is done with stage s ^ 1
+            if (t < t_last) issue(t + 1, s ^ 1);
+            const LDS char *kr = smem + s * kDqStage;
+            const LDS char *kt = kr + G::TILE_BYTES;
+            const LDS char *vr = kr + 2 * G::TILE_BYTES;
+            const bool full = t >= t_in_lo && t < t_in_hi && (t + 1) * BN <= S;
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                f32x16 sa = f32x16{}, da = f32x16{};
+#pragma unroll
+                for (int c = 0; c < NDC; ++c) {
+                    sa = Elem<T>::mma(read_rows(kr, o, sb, c), qf[c], sa);
+                    da = Elem<T>::mma(read_rows(vr, o, sb, c), df[c], da);
+                }
+                // element e: key t*BN + 32sb + 8(e/4) + 4g + e%4, query qi
+                uint32_t dsp[8];
+#pragma unroll
+                for (int e = 0; e < 16; e += 2) {
+                    float ds[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int j = t * BN + 32 * sb + 8 * ((e + u) >> 2) + 4 * g + ((e + u) & 3);
+                        const bool ok = full || (j < S && j >= qi - p.win_lo && j <= qi + p.win_hi);
+                        const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sa[e + u], c2, -lse2))
+                                            : 0.0f;
+                        ds[u] = pr * (da[e + u] - drow);
+                    }
+                    dsp[e >> 1] = Elem<T>::pack(ds[0], ds[1]);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        acc[db] = Elem<T>::mma(read_tr(kt, o, db, 2 * sb + hh), half_of(dsp, hh),
+                                               acc[db]);
+            }
+        }
+        if (qi < S)
+            store_rows(static_cast<uint16_t *>(p.dq) + head, qi, g, acc, p.scale);
+    }
+
+    // ---- dK, dV -----------------------------------------------------------------
+    // LDS per stage: Q rows, Q (transposed), dO rows, dO (transposed), then the
+    // tile's LSE * log2(e) and D_i (BN floats each).
+    static constexpr uint32_t kKvStage = 4 * G::TILE_BYTES + 2 * BN * 4;
+
+    static __device__ void dkdv(const BwdParams &p, LDS char *smem) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int l32 = lane & 31, g = lane >> 5;
+        const int S = p.S;
+        const int ntk = (S + kBwdRows - 1) / kBwdRows;
+        const int bh = (int)blockIdx.x / ntk;
+        const int kt = (int)blockIdx.x - bh * ntk;  // under causal masks the first keys see most rows
+        const int k0 = kt * kBwdRows, kj = k0 + 32 * wave + l32;
+        const int64_t head = (int64_t)bh * S * D;
+        const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
+        const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
+        const uint16_t *vh = static_cast<const uint16_t *>(p.v) + head;
+        const uint16_t *doh = static_cast<const uint16_t *>(p.dout) + head;
+        const float *lse_h = p.lse + (int64_t)bh * S;
+        const float *dot_h = p.rowdot + (int64_t)bh * S;
+
+        vec8 kf[NDC], vf[NDC];
+        load_frags(kh, kj, S, g, kf);
+        load_frags(vh, kj, S, g, vf);
+        const float c2 = p.scale * kLog2e;
+
+        // rows that see any of the workgroup's keys: j - win_hi <= i <= j + win_lo
+        const int klast = min(k0 + kBwdRows - 1, S - 1);
+        const int u_first = max(0, k0 - p.win_hi) / BN;
+        const int u_last = min(S - 1, klast + p.win_lo) / BN;
+        // query tiles that see every key of the workgroup
+        const int u_in_lo = (max(0, klast - p.win_hi) + BN - 1) / BN;
+        const int u_in_hi = (min(S - 1, k0 + p.win_lo) + 1) / BN;
+
+        Offs o;
+        make_offs(o, lane);
+        const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+        auto issue = [&](int u, int s) {
+            const uint32_t st = sbase + s * kKvStage;
+            load_tile<kRowSwz>(qh, u * BN, S, st, wave, lane);
+            load_tile<kTrSwz>(qh, u * BN, S, st + G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz>(doh, u * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
+            load_tile<kTrSwz>(doh, u * BN, S, st + 3 * G::TILE_BYTES, wave, lane);
+        };
+        // the tile's LSE (base 2) and D_i: fetched by the first BN threads,
+        // stored into the stage's arrays once they arrive
+        auto fetch_vec = [&](int u, float &l2, float &dr) {
+            const int i = u * BN + (int)threadIdx.x;
+            l2 = i < S ? lse_h[i] * kLog2e : 0.0f;
+            dr = i < S ? dot_h[i] : 0.0f;
+        };
+        auto put_vec = [&](int s, float l2, float dr) {
+            LDS float *v = reinterpret_cast<LDS float *>(smem + s * kKvStage + 4 * G::TILE_BYTES);
+            v[threadIdx.x] = l2;
+            v[BN + threadIdx.x] = dr;
+        };
+
+        f32x16 dva[NDB], dka[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dva[db] = dka[db] = f32x16{};
+        issue(u_first, 0);
+        if (threadIdx.x < BN) {
+            float l2, dr;
+            fetch_vec(u_first, l2, dr);
+            put_vec(0, l2, dr);
+        }
+        for (int u = u_first; u <= u_last; ++u) {
+            const int s = (u - u_first) & 1;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // tile u and its vectors are in LDS; stage s ^ 1 is free
+            float nl2 = 0.0f, ndr = 0.0f;
+            const bool more = u < u_last;
+            if (more) {
+                issue(u + 1, s ^ 1);
+                if (threadIdx.x < BN) fetch_vec(u + 1, nl2, ndr);
+            }
+            const LDS char *qr = smem + s * kKvStage;
+            const LDS char *qtr = qr + G::TILE_BYTES;
+            const LDS char *dor = qr + 2 * G::TILE_BYTES;
+            const LDS char *dotr = qr + 3 * G::TILE_BYTES;
+            const LDS float *vl = reinterpret_cast<const LDS float *>(qr + 4 * G::TILE_BYTES);
+            const bool full = u >= u_in_lo && u < u_in_hi && (u + 1) * BN <= S && klast < S &&
+                              k0 + kBwdRows <= S;
+#pragma unroll
+            for (int sb = 0; sb < NSB; ++sb) {
+                f32x16 sa = f32x16{}, da = f32x16{};
+#pragma unroll
+                for (int c = 0; c < NDC; ++c) {
+                    sa = Elem<T>::mma(read_rows(qr, o, sb, c), kf[c], sa);
+                    da = Elem<T>::mma(read_rows(dor, o, sb, c), vf[c], da);
+                }
+                // element e: query u*BN + 32sb + 8(e/4) + 4g + e%4, key kj
+                uint32_t pp[8], dsp[8];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int r = 32 * sb + 8 * a + 4 * g;  // row of element 4a within the tile
+                    const f32x4 l4 = *reinterpret_cast<const LDS f32x4 *>(vl + r);
+                    const f32x4 d4 = *reinterpret_cast<const LDS f32x4 *>(vl + BN + r);
+                    const float lv[4] = {l4[0], l4[1], l4[2], l4[3]};
+                    const float dv4[4] = {d4[0], d4[1], d4[2], d4[3]};
+                    float pr[4], ds[4];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const int i = u * BN + r + w;
+                        const bool ok = full || (i < S && kj < S && kj >= i - p.win_lo &&
+                                                 kj <= i + p.win_hi);
+                        pr[w] = ok ? __builtin_amdgcn_exp2f(fmaf(sa[4 * a + w], c2, -lv[w]))
+                                   : 0.0f;
+                        ds[w] = pr[w] * (da[4 * a + w] - dv4[w]);
+                    }
+                    pp[2 * a] = Elem<T>::pack(pr[0], pr[1]);
+                    pp[2 * a + 1] = Elem<T>::pack(pr[2], pr[3]);
+                    dsp[2 * a] = Elem<T>::pack(ds[0], ds[1]);
+                    dsp[2 * a + 1] = Elem<T>::pack(ds[2], ds[3]);
+                }
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        dva[db] = Elem<T>::mma(read_tr(dotr, o, db, 2 * sb + hh), half_of(pp, hh),
+                                               dva[db]);
+                        dka[db] = Elem<T>::mma(read_tr(qtr, o, db, 2 * sb + hh), half_of(dsp, hh),
+                                               dka[db]);
+                    }
+            }
+            if (more && threadIdx.x < BN) put_vec(s ^ 1, nl2, ndr);
+        }
+        if (kj < S) {
+            store_rows(static_cast<uint16_t *>(p.dv) + head, kj, g, dva, 1.0f);
+            store_rows(static_cast<uint16_t *>(p.dk) + head, kj, g, dka, p.scale);
+        }
+    }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * Bwd<T, D>::kDqStage];
+    Bwd<T, D>::dq(p, (LDS char *)smem);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * Bwd<T, D>::kKvStage];
+    Bwd<T, D>::dkdv(p, (LDS char *)smem);
+}
+
+// D_i = dO_i . O_i in fp32: D/8 threads per row, 8 elements each, summed
+// across the row's threads with lane exchanges.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fa_bwd_rowdot_kernel(BwdParams p) {
+    typedef typename Elem<T>::vec8 vec8;
+    constexpr int TPR = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / TPR;
+    const int part = (int)(gid % TPR);
+    const int64_t rows = (int64_t)p.B * p.H * p.S;
+    float acc = 0.0f;
+    if (row < rows) {
+        const int64_t off = row * D + 8 * part;
+        const vec8 a = __builtin_bit_cast(
+            vec8, *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.dout) + off));
+        const vec8 b = __builtin_bit_cast(
+            vec8, *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.o) + off));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+    if (row < rows && part == 0) p.rowdot[row] = acc;
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
+    void *args[] = {const_cast<BwdParams *>(&p)};
+    const int64_t rows = (int64_t)p.B * p.H * p.S;
+    const int64_t rd_blocks = (rows * (D / 8) + 255) / 256;
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_rowdot_kernel<T, D>),
+                                   dim3((unsigned)rd_blocks), dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = (int64_t)p.B * p.H * ((p.S + kBwdRows - 1) / kBwdRows);
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_kernel<T, D>),
+                        dim3((unsigned)tiles), dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D>),
+                           dim3((unsigned)tiles), dim3(kBwdThreads), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams &p, int D, int dtype, hipStream_t stream) {
+    if (D == 128) return dtype == 0 ? launch_bwd_t<_Float16, 128>(p, stream)
+                                    : launch_bwd_t<__bf16, 128>(p, stream);
+    if (D == 64) return dtype == 0 ? launch_bwd_t<_Float16, 64>(p, stream)
+                                   : launch_bwd_t<__bf16, 64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -74,6 +74,20 @@ constexpr int kMaxPackedSeqs = 1024;
 // Enqueue the kernel for head dimension D and dtype (0 fp16, 1 bf16).
 hipError_t launch_fwd(const FwdParams &p, int D, int dtype, hipStream_t stream);
 
+// ---- backward -------------------------------------------------------------------
+struct BwdParams {
+    const void *q, *k, *v, *o, *dout;  // [B, H, S, D]
+    const float *lse;                  // [B, H, S], natural log (the forward's)
+    float *rowdot;                     // workspace [B, H, S]: D_i = dO_i . O_i
+    void *dq, *dk, *dv;                // [B, H, S, D]
+    int B, H, S;
+    int win_lo, win_hi;                // as in FwdParams
+    float scale;                       // signed
+};
+
+// Enqueue the three backward kernels (row dots, dK/dV, dQ).
+hipError_t launch_bwd(const BwdParams &p, int D, int dtype, hipStream_t stream);
+
 // ---- new query rows against a key/value cache ---------------------------------
 // Keys per tile of the cache kernel.
 constexpr int kDecodeBN = 32;
