@@ -10,7 +10,9 @@ With ``--workload decode_*`` one step is one fa_decode call (new query rows
 against a key/value cache, HBM-bound): the line reports GB/s of algorithmic
 bytes against the 8 TB/s HBM peak instead. With ``--workload varlen_*`` one
 step is one fa_fwd_varlen call over a packed batch of ragged sequences
-(TFLOP/s over the visible pairs of every sequence).
+(TFLOP/s over the visible pairs of every sequence). With ``--workload
+bwd_<forward workload>`` one step is one fa_bwd call (10 * D FLOPs per
+visible pair).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-seconds T]
 """
@@ -34,6 +36,9 @@ KERNEL_SOURCES = ["tiled_attention_11_amd/csrc/fa_kernel.hip",
                   "tiled_attention_11_amd/csrc/fa_internal.h",
                   "tiled_attention_11_amd/csrc/fa_device.h"]
 ROPE_SOURCES = KERNEL_SOURCES + ["tiled_attention_11_amd/csrc/fa_rope.hip"]
+BWD_SOURCES = ["tiled_attention_11_amd/csrc/fa_bwd.hip",
+               "tiled_attention_11_amd/csrc/fa_internal.h",
+               "tiled_attention_11_amd/csrc/fa_device.h"]
 DECODE_SOURCES = ["tiled_attention_11_amd/csrc/fa_decode.hip",
                   "tiled_attention_11_amd/csrc/fa_internal.h",
                   "tiled_attention_11_amd/csrc/fa_device.h"]
@@ -389,6 +394,120 @@ def bench_varlen(args, name):
     print(json.dumps(result), flush=True)
 
 
+def bench_bwd(args, name):
+    """One step = one fa_bwd call (the forward's O and LSE computed beforehand)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import tiled_attention_11_amd as fa
+
+    fwd_name = name[len("bwd_"):]
+    w = synth.WORKLOADS[fwd_name]
+    B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
+    wl, wr = w["window"]
+    m = fa._mask_code(w["mask"])
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v = synth.workload_inputs(fwd_name)
+    do, _, _ = synth.make_qkv(B, H, S, D, dtype, w["seed"] + 1000)
+    tq, tk, tv, tdo = (torch.from_numpy(x.view(np.int16)).view(tdt).to(dev)
+                       for x in (q, k, v, do))
+    o, lse = fa.forward(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr))
+    dq, dk, dv = (torch.empty_like(tq) for _ in range(3))
+    ws = torch.empty(int(fa.fa_bwd_workspace_bytes(B, H, S)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] {name}: inputs and forward ready in {time.perf_counter() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+
+    def step():
+        fa.backward(tq, tk, tv, o, lse, tdo, scale=w["scale"], mask=w["mask"], window=(wl, wr),
+                    dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]) * 1e-3
+    avg_s = evs[0].elapsed_time(evs[-1]) * 1e-3 / args.steps
+    print(f"[bench] timed {args.steps} steps: avg {avg_s * 1e6:.1f} us, median "
+          f"{np.median(per) * 1e6:.1f} us", file=sys.stderr, flush=True)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+    flops = fa.fa_bwd_flops(B, H, S, D, m, wl, wr)
+    tflops = flops / avg_s / 1e12
+    result = {
+        "metric": f"attention backward TFLOP/s and % of fp16 MFMA peak, {fwd_name}",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(avg_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{name}: fa_bwd (row dots + dK/dV kernel + dQ kernel) at B={B} H={H} "
+                         f"S={S} D={D} {dtype} {w['mask']} scale={w['scale']:.6g}, dO standard "
+                         "normal; O and LSE from fa_fwd outside the timed region"),
+            "B": B, "H": H, "S": S, "D": D, "mask": w["mask"], "window": [wl, wr],
+            "flops_per_step": flops,
+        },
+        "pct_of_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 2),
+        "median_launch_us": round(float(np.median(per)) * 1e6, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
+            "traffic": counted_traffic(name, sources=BWD_SOURCES),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        orc = oracle.load()
+        got = [g.cpu().view(torch.int16).numpy().view(np.uint16) for g in (dq, dk, dv)]
+        from tests.parity import decode as dec
+        heads, t_used, worst = 0, 0.0, 0.0
+        u = 2.0 ** -11 if dtype == "f16" else 2.0 ** -8
+        while heads < B * H and t_used < args.cpu_seconds:
+            b, h = divmod(heads * 37 % (B * H), H)  # spread over the batch
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            t1 = time.perf_counter()
+            refs, mags = orc.attention_bwd(q[sl], k[sl], v[sl], do[sl], dtype, w["scale"],
+                                           w["mask"], (wl, wr))
+            t_used += time.perf_counter() - t1
+            for g, r, mg in zip(got, refs, mags):
+                err = np.abs(dec(g[sl], dtype).reshape(r.shape) - r)
+                worst = max(worst, float((err / (2 * u * mg + 2.0 ** -10 * np.abs(r) + 2.0 ** -24)).max()))
+            heads += 1
+        per_head = flops // (B * H)
+        result["cpu_baseline"] = {
+            "value": round(heads * per_head / t_used / 1e12, 6), "unit": "TFLOP/s",
+            "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"{heads} whole heads of the same workload, {t_used:.2f} s wall, fp64",
+        }
+        result["parity_sample"] = {"heads": heads, "worst_error_over_bound": round(worst, 4),
+                                   "pass": worst <= 1.0}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,6 +539,8 @@ def main():
         return bench_decode(args, name)
     if name in synth.VARLEN_WORKLOADS:
         return bench_varlen(args, name)
+    if name.startswith("bwd_") and name[len("bwd_"):] in synth.WORKLOADS:
+        return bench_bwd(args, name)
     w = synth.WORKLOADS[name]
     B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
     wl, wr = w["window"]

@@ -15,7 +15,7 @@
 //
 // gfx950 design: three kernels.
 //  * fa_bwd_rowdot: D_i = dO_i . O_i (fp32) into the caller's workspace.
-//  * fa_bwd_dq: a workgroup of 4 waves owns 128 query rows (32 per wave, a
+//  * fa_bwd_dq: a workgroup of 8 waves owns 256 query rows (32 per wave, a
 //    row per lane as in the forward) and streams the visible 64-key tiles of
 //    K and V through LDS (direct HBM -> LDS DMA, two stages). Per 32-key
 //    block: S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16 (Q^T, dO^T
@@ -23,7 +23,7 @@
 //    layout (one query per lane: its LSE and D_i are scalars), and
 //    dQ^T += K^T dS^T with K^T from transposing LDS reads
 //    (ds_read_b64_tr_b16) and dS^T straight from the accumulator.
-//  * fa_bwd_dkdv: the mirror image: a workgroup owns 128 keys (K^T, V^T
+//  * fa_bwd_dkdv: the mirror image: a workgroup of 4 waves owns 128 keys (K^T, V^T
 //    fragments in registers, a key per lane) and streams the 64-query tiles
 //    of Q and dO that see them, with their LSE and D_i staged in LDS. Per
 //    32-query block: S = Q K^T and dP = dO V^T, then P and dS (a query per
@@ -45,9 +45,12 @@ namespace {
 
 using namespace dev;
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kBwdRows = 32 * kBwdWaves;  // fixed rows (queries or keys) per workgroup
+// Waves per workgroup (each owns 32 fixed rows: queries or keys). The dQ
+// kernel fits two waves per SIMD (under 256 registers each), which lets one
+// wave's VALU work run beside the other's MFMAs; the dK/dV kernel holds twice
+// the accumulators and runs one wave per SIMD.
+constexpr int kDqWaves = 8;
+constexpr int kKvWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D> struct BGeom {
@@ -57,7 +60,7 @@ template <int D> struct BGeom {
     static constexpr int TILE_BYTES = BN * RB;     // 16 KiB (D = 128), 8 KiB (D = 64)
     static constexpr int ROWS_PER_KB = 1024 / RB;  // rows per 1 KiB DMA block
     static constexpr int NBLK = TILE_BYTES / 1024; // DMA blocks per tile
-    static_assert(NBLK % kBwdWaves == 0, "DMA split");
+    static_assert(NBLK % kDqWaves == 0 && NBLK % kKvWaves == 0, "DMA split");
 };
 
 // Swizzles of a tile: row-read (MFMA A operand of rows) or transposed-read.
@@ -75,15 +78,15 @@ struct Bwd {
     // Stream rows r0 .. r0 + BN - 1 of the [S, D] head at h into the LDS tile
     // at byte address slot, with the given swizzle (this wave's share of the
     // 1 KiB DMA blocks). Rows past S read as zero.
-    template <int SW>
+    template <int SW, int NW>
     static __device__ __forceinline__ void load_tile(const uint16_t *h, int r0, int S,
                                                      uint32_t slot, int wave, int lane) {
         const i32x4 rsrc =
             buffer_rsrc(h + (int64_t)r0 * D, r0 < S ? (uint32_t)(S - r0) * G::RB : 0u);
         const int pc = lane % G::CPR;
 #pragma unroll
-        for (int i = 0; i < G::NBLK / kBwdWaves; ++i) {
-            const int b = i * kBwdWaves + wave;
+        for (int i = 0; i < G::NBLK / NW; ++i) {
+            const int b = i * NW + wave;
             const int row = b * G::ROWS_PER_KB + lane / G::CPR;
             const int lc = SW == kRowSwz ? kchunk<D>(pc, row) : vchunk<D>(pc, row);
             dma16(rsrc, slot + (uint32_t)b * 1024u, (uint32_t)(row * G::RB + lc * 16));
@@ -171,10 +174,11 @@ struct Bwd {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int l32 = lane & 31, g = lane >> 5;
         const int S = p.S;
-        const int ntq = (S + kBwdRows - 1) / kBwdRows;
+        constexpr int ROWS = 32 * kDqWaves;
+        const int ntq = (S + ROWS - 1) / ROWS;
         const int bh = (int)blockIdx.x / ntq;
         const int qt = ntq - 1 - ((int)blockIdx.x - bh * ntq);  // longest rows first
-        const int q0 = qt * kBwdRows, qi = q0 + 32 * wave + l32;
+        const int q0 = qt * ROWS, qi = q0 + 32 * wave + l32;
         const int64_t head = (int64_t)bh * S * D;
         const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
         const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
@@ -188,7 +192,7 @@ struct Bwd {
         const float drow = qi < S ? p.rowdot[(int64_t)bh * S + qi] : 0.0f;
         const float c2 = p.scale * kLog2e;
 
-        const int qlast = min(q0 + kBwdRows - 1, S - 1);
+        const int qlast = min(q0 + ROWS - 1, S - 1);
         const int t_first = max(0, q0 - p.win_lo) / BN;
         const int t_last = min(S - 1, qlast + p.win_hi) / BN;
         // tiles visible in full from every row of the workgroup
@@ -200,9 +204,9 @@ struct Bwd {
         const uint32_t sbase = (uint32_t)(uintptr_t)smem;
         auto issue = [&](int t, int s) {
             const uint32_t st = sbase + s * kDqStage;
-            load_tile<kRowSwz>(kh, t * BN, S, st, wave, lane);
-            load_tile<kTrSwz>(kh, t * BN, S, st + G::TILE_BYTES, wave, lane);
-            load_tile<kRowSwz>(vh, t * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz, kDqWaves>(kh, t * BN, S, st, wave, lane);
+            load_tile<kTrSwz, kDqWaves>(kh, t * BN, S, st + G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz, kDqWaves>(vh, t * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
         };
 
         f32x16 acc[NDB];
@@ -263,10 +267,11 @@ struct Bwd {
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int l32 = lane & 31, g = lane >> 5;
         const int S = p.S;
-        const int ntk = (S + kBwdRows - 1) / kBwdRows;
+        constexpr int ROWS = 32 * kKvWaves;
+        const int ntk = (S + ROWS - 1) / ROWS;
         const int bh = (int)blockIdx.x / ntk;
         const int kt = (int)blockIdx.x - bh * ntk;  // under causal masks the first keys see most rows
-        const int k0 = kt * kBwdRows, kj = k0 + 32 * wave + l32;
+        const int k0 = kt * ROWS, kj = k0 + 32 * wave + l32;
         const int64_t head = (int64_t)bh * S * D;
         const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
         const uint16_t *kh = static_cast<const uint16_t *>(p.k) + head;
@@ -281,7 +286,7 @@ struct Bwd {
         const float c2 = p.scale * kLog2e;
 
         // rows that see any of the workgroup's keys: j - win_hi <= i <= j + win_lo
-        const int klast = min(k0 + kBwdRows - 1, S - 1);
+        const int klast = min(k0 + ROWS - 1, S - 1);
         const int u_first = max(0, k0 - p.win_hi) / BN;
         const int u_last = min(S - 1, klast + p.win_lo) / BN;
         // query tiles that see every key of the workgroup
@@ -293,10 +298,10 @@ struct Bwd {
         const uint32_t sbase = (uint32_t)(uintptr_t)smem;
         auto issue = [&](int u, int s) {
             const uint32_t st = sbase + s * kKvStage;
-            load_tile<kRowSwz>(qh, u * BN, S, st, wave, lane);
-            load_tile<kTrSwz>(qh, u * BN, S, st + G::TILE_BYTES, wave, lane);
-            load_tile<kRowSwz>(doh, u * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
-            load_tile<kTrSwz>(doh, u * BN, S, st + 3 * G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz, kKvWaves>(qh, u * BN, S, st, wave, lane);
+            load_tile<kTrSwz, kKvWaves>(qh, u * BN, S, st + G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz, kKvWaves>(doh, u * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
+            load_tile<kTrSwz, kKvWaves>(doh, u * BN, S, st + 3 * G::TILE_BYTES, wave, lane);
         };
         // the tile's LSE (base 2) and D_i: fetched by the first BN threads,
         // stored into the stage's arrays once they arrive
@@ -336,7 +341,7 @@ struct Bwd {
             const LDS char *dotr = qr + 3 * G::TILE_BYTES;
             const LDS float *vl = reinterpret_cast<const LDS float *>(qr + 4 * G::TILE_BYTES);
             const bool full = u >= u_in_lo && u < u_in_hi && (u + 1) * BN <= S && klast < S &&
-                              k0 + kBwdRows <= S;
+                              k0 + ROWS <= S;
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
                 f32x16 sa = f32x16{}, da = f32x16{};
@@ -389,13 +394,13 @@ struct Bwd {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * kDqWaves, 1) void fa_bwd_dq_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * Bwd<T, D>::kDqStage];
     Bwd<T, D>::dq(p, (LDS char *)smem);
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kBwdThreads, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * kKvWaves, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * Bwd<T, D>::kKvStage];
     Bwd<T, D>::dkdv(p, (LDS char *)smem);
 }
@@ -433,12 +438,14 @@ hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_rowdot_kernel<T, D>),
                                    dim3((unsigned)rd_blocks), dim3(256), args, 0, stream);
     if (e != hipSuccess) return e;
-    const int64_t tiles = (int64_t)p.B * p.H * ((p.S + kBwdRows - 1) / kBwdRows);
+    const int64_t bh = (int64_t)p.B * p.H;
+    const int64_t kv_tiles = bh * ((p.S + 32 * kKvWaves - 1) / (32 * kKvWaves));
     e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_kernel<T, D>),
-                        dim3((unsigned)tiles), dim3(kBwdThreads), args, 0, stream);
+                        dim3((unsigned)kv_tiles), dim3(64 * kKvWaves), args, 0, stream);
     if (e != hipSuccess) return e;
+    const int64_t q_tiles = bh * ((p.S + 32 * kDqWaves - 1) / (32 * kDqWaves));
     return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D>),
-                           dim3((unsigned)tiles), dim3(kBwdThreads), args, 0, stream);
+                           dim3((unsigned)q_tiles), dim3(64 * kDqWaves), args, 0, stream);
 }
 
 }  // namespace
