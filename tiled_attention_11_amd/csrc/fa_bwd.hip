@@ -45,22 +45,20 @@ namespace {
 
 using namespace dev;
 
-// Waves per workgroup (each owns 32 fixed rows: queries or keys). The dQ
-// kernel fits two waves per SIMD (under 256 registers each), which lets one
-// wave's VALU work run beside the other's MFMAs; the dK/dV kernel holds twice
-// the accumulators and runs one wave per SIMD.
+// Waves per workgroup (each owns 32 fixed rows: queries or keys). Both
+// kernels fit two waves per SIMD (under 256 registers each), which lets one
+// wave's VALU work run beside the other's MFMAs.
 constexpr int kDqWaves = 8;
-constexpr int kKvWaves = 4;
+constexpr int kKvWaves = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D> struct BGeom {
-    static constexpr int BN = 64;                  // streamed rows per tile
+template <int D, int BN_> struct BGeom {
+    static constexpr int BN = BN_;                 // streamed rows per tile
     static constexpr int RB = 2 * D;               // bytes per row
     static constexpr int CPR = RB / 16;            // 16-byte chunks per row
-    static constexpr int TILE_BYTES = BN * RB;     // 16 KiB (D = 128), 8 KiB (D = 64)
+    static constexpr int TILE_BYTES = BN * RB;
     static constexpr int ROWS_PER_KB = 1024 / RB;  // rows per 1 KiB DMA block
     static constexpr int NBLK = TILE_BYTES / 1024; // DMA blocks per tile
-    static_assert(NBLK % kDqWaves == 0 && NBLK % kKvWaves == 0, "DMA split");
 };
 
 // Swizzles of a tile: row-read (MFMA A operand of rows) or transposed-read.
@@ -68,28 +66,32 @@ enum { kRowSwz = 0, kTrSwz = 1 };
 
 template <typename T, int D>
 struct Bwd {
-    typedef BGeom<D> G;
+    typedef BGeom<D, 64> G;     // dQ kernel: 64-key tiles
+    typedef BGeom<D, 32> GQ;    // dK/dV kernel: 32-query tiles
     typedef typename Elem<T>::vec8 vec8;
     static constexpr int BN = G::BN;
     static constexpr int NDC = D / 16;   // 16-dim chunks of a dims contraction
     static constexpr int NDB = D / 32;   // 32-dim output blocks
     static constexpr int NSB = BN / 32;  // 32-row blocks of a streamed tile
 
-    // Stream rows r0 .. r0 + BN - 1 of the [S, D] head at h into the LDS tile
-    // at byte address slot, with the given swizzle (this wave's share of the
-    // 1 KiB DMA blocks). Rows past S read as zero.
-    template <int SW, int NW>
+    // Stream rows r0 .. r0 + NR - 1 of the [S, D] head at h into the LDS
+    // tile at byte address slot, with the given swizzle (blocks wave,
+    // wave + NW, ... of its 1 KiB DMA blocks are this wave's). Rows past S
+    // read as zero.
+    template <int SW, int NW, int NR>
     static __device__ __forceinline__ void load_tile(const uint16_t *h, int r0, int S,
                                                      uint32_t slot, int wave, int lane) {
-        const i32x4 rsrc =
-            buffer_rsrc(h + (int64_t)r0 * D, r0 < S ? (uint32_t)(S - r0) * G::RB : 0u);
-        const int pc = lane % G::CPR;
+        constexpr int RB = 2 * D, CPR = RB / 16, RPK = 1024 / RB, NBLK = NR * RB / 1024;
+        const i32x4 rsrc = buffer_rsrc(h + (int64_t)r0 * D, r0 < S ? (uint32_t)(S - r0) * RB : 0u);
+        const int pc = lane % CPR;
 #pragma unroll
-        for (int i = 0; i < G::NBLK / NW; ++i) {
+        for (int i = 0; i < (NBLK + NW - 1) / NW; ++i) {
             const int b = i * NW + wave;
-            const int row = b * G::ROWS_PER_KB + lane / G::CPR;
-            const int lc = SW == kRowSwz ? kchunk<D>(pc, row) : vchunk<D>(pc, row);
-            dma16(rsrc, slot + (uint32_t)b * 1024u, (uint32_t)(row * G::RB + lc * 16));
+            if (NBLK % NW == 0 || b < NBLK) {
+                const int row = b * RPK + lane / CPR;
+                const int lc = SW == kRowSwz ? kchunk<D>(pc, row) : vchunk<D>(pc, row);
+                dma16(rsrc, slot + (uint32_t)b * 1024u, (uint32_t)(row * RB + lc * 16));
+            }
         }
     }
 
@@ -204,9 +206,9 @@ struct Bwd {
         const uint32_t sbase = (uint32_t)(uintptr_t)smem;
         auto issue = [&](int t, int s) {
             const uint32_t st = sbase + s * kDqStage;
-            load_tile<kRowSwz, kDqWaves>(kh, t * BN, S, st, wave, lane);
-            load_tile<kTrSwz, kDqWaves>(kh, t * BN, S, st + G::TILE_BYTES, wave, lane);
-            load_tile<kRowSwz, kDqWaves>(vh, t * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz, kDqWaves, BN>(kh, t * BN, S, st, wave, lane);
+            load_tile<kTrSwz, kDqWaves, BN>(kh, t * BN, S, st + G::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz, kDqWaves, BN>(vh, t * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
         };
 
         f32x16 acc[NDB];
@@ -258,9 +260,13 @@ struct Bwd {
     }
 
     // ---- dK, dV -----------------------------------------------------------------
-    // LDS per stage: Q rows, Q (transposed), dO rows, dO (transposed), then the
-    // tile's LSE * log2(e) and D_i (BN floats each).
-    static constexpr uint32_t kKvStage = 4 * G::TILE_BYTES + 2 * BN * 4;
+    // LDS: the V rows of the workgroup's keys (row swizzle; the B operand of
+    // dP = dO V^T is read from there, which keeps the wave under 256
+    // registers), then per stage: Q rows, Q (transposed), dO rows, dO
+    // (transposed), and the tile's LSE * log2(e) and D_i (32 floats each).
+    static constexpr int QB = GQ::BN;  // query rows per streamed tile
+    static constexpr uint32_t kKvV = 32 * kKvWaves * GQ::RB;
+    static constexpr uint32_t kKvStage = 4 * GQ::TILE_BYTES + 2 * QB * 4;
 
     static __device__ void dkdv(const BwdParams &p, LDS char *smem) {
         const int lane = threadIdx.x & 63;
@@ -280,47 +286,50 @@ struct Bwd {
         const float *lse_h = p.lse + (int64_t)bh * S;
         const float *dot_h = p.rowdot + (int64_t)bh * S;
 
-        vec8 kf[NDC], vf[NDC];
+        vec8 kf[NDC];
         load_frags(kh, kj, S, g, kf);
-        load_frags(vh, kj, S, g, vf);
         const float c2 = p.scale * kLog2e;
 
         // rows that see any of the workgroup's keys: j - win_hi <= i <= j + win_lo
         const int klast = min(k0 + ROWS - 1, S - 1);
-        const int u_first = max(0, k0 - p.win_hi) / BN;
-        const int u_last = min(S - 1, klast + p.win_lo) / BN;
+        const int u_first = max(0, k0 - p.win_hi) / QB;
+        const int u_last = min(S - 1, klast + p.win_lo) / QB;
         // query tiles that see every key of the workgroup
-        const int u_in_lo = (max(0, klast - p.win_hi) + BN - 1) / BN;
-        const int u_in_hi = (min(S - 1, k0 + p.win_lo) + 1) / BN;
+        const int u_in_lo = (max(0, klast - p.win_hi) + QB - 1) / QB;
+        const int u_in_hi = (min(S - 1, k0 + p.win_lo) + 1) / QB;
+        const bool keys_in = k0 + ROWS <= S;
 
         Offs o;
         make_offs(o, lane);
         const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+        const LDS char *vw = smem + wave * 32 * GQ::RB;  // this wave's V rows
         auto issue = [&](int u, int s) {
-            const uint32_t st = sbase + s * kKvStage;
-            load_tile<kRowSwz, kKvWaves>(qh, u * BN, S, st, wave, lane);
-            load_tile<kTrSwz, kKvWaves>(qh, u * BN, S, st + G::TILE_BYTES, wave, lane);
-            load_tile<kRowSwz, kKvWaves>(doh, u * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
-            load_tile<kTrSwz, kKvWaves>(doh, u * BN, S, st + 3 * G::TILE_BYTES, wave, lane);
+            const uint32_t st = sbase + kKvV + s * kKvStage;
+            load_tile<kRowSwz, kKvWaves, QB>(qh, u * QB, S, st, wave, lane);
+            load_tile<kTrSwz, kKvWaves, QB>(qh, u * QB, S, st + GQ::TILE_BYTES, wave, lane);
+            load_tile<kRowSwz, kKvWaves, QB>(doh, u * QB, S, st + 2 * GQ::TILE_BYTES, wave, lane);
+            load_tile<kTrSwz, kKvWaves, QB>(doh, u * QB, S, st + 3 * GQ::TILE_BYTES, wave, lane);
         };
-        // the tile's LSE (base 2) and D_i: fetched by the first BN threads,
+        // the tile's LSE (base 2) and D_i: fetched by the first QB threads,
         // stored into the stage's arrays once they arrive
         auto fetch_vec = [&](int u, float &l2, float &dr) {
-            const int i = u * BN + (int)threadIdx.x;
+            const int i = u * QB + (int)threadIdx.x;
             l2 = i < S ? lse_h[i] * kLog2e : 0.0f;
             dr = i < S ? dot_h[i] : 0.0f;
         };
         auto put_vec = [&](int s, float l2, float dr) {
-            LDS float *v = reinterpret_cast<LDS float *>(smem + s * kKvStage + 4 * G::TILE_BYTES);
+            LDS float *v =
+                reinterpret_cast<LDS float *>(smem + kKvV + s * kKvStage + 4 * GQ::TILE_BYTES);
             v[threadIdx.x] = l2;
-            v[BN + threadIdx.x] = dr;
+            v[QB + threadIdx.x] = dr;
         };
 
         f32x16 dva[NDB], dka[NDB];
 #pragma unroll
         for (int db = 0; db < NDB; ++db) dva[db] = dka[db] = f32x16{};
+        load_tile<kRowSwz, kKvWaves, ROWS>(vh, k0, S, sbase, wave, lane);
         issue(u_first, 0);
-        if (threadIdx.x < BN) {
+        if (threadIdx.x < QB) {
             float l2, dr;
             fetch_vec(u_first, l2, dr);
             put_vec(0, l2, dr);
@@ -333,58 +342,51 @@ struct Bwd {
             const bool more = u < u_last;
             if (more) {
                 issue(u + 1, s ^ 1);
-                if (threadIdx.x < BN) fetch_vec(u + 1, nl2, ndr);
+                if (threadIdx.x < QB) fetch_vec(u + 1, nl2, ndr);
             }
-            const LDS char *qr = smem + s * kKvStage;
-            const LDS char *qtr = qr + G::TILE_BYTES;
-            const LDS char *dor = qr + 2 * G::TILE_BYTES;
-            const LDS char *dotr = qr + 3 * G::TILE_BYTES;
-            const LDS float *vl = reinterpret_cast<const LDS float *>(qr + 4 * G::TILE_BYTES);
-            const bool full = u >= u_in_lo && u < u_in_hi && (u + 1) * BN <= S && klast < S &&
-                              k0 + ROWS <= S;
+            const LDS char *qr = smem + kKvV + s * kKvStage;
+            const LDS char *qtr = qr + GQ::TILE_BYTES;
+            const LDS char *dor = qr + 2 * GQ::TILE_BYTES;
+            const LDS char *dotr = qr + 3 * GQ::TILE_BYTES;
+            const LDS float *vl = reinterpret_cast<const LDS float *>(qr + 4 * GQ::TILE_BYTES);
+            const bool full = u >= u_in_lo && u < u_in_hi && (u + 1) * QB <= S && keys_in;
+            f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
-            for (int sb = 0; sb < NSB; ++sb) {
-                f32x16 sa = f32x16{}, da = f32x16{};
-#pragma unroll
-                for (int c = 0; c < NDC; ++c) {
-                    sa = Elem<T>::mma(read_rows(qr, o, sb, c), kf[c], sa);
-                    da = Elem<T>::mma(read_rows(dor, o, sb, c), vf[c], da);
-                }
-                // element e: query u*BN + 32sb + 8(e/4) + 4g + e%4, key kj
-                uint32_t pp[8], dsp[8];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int r = 32 * sb + 8 * a + 4 * g;  // row of element 4a within the tile
-                    const f32x4 l4 = *reinterpret_cast<const LDS f32x4 *>(vl + r);
-                    const f32x4 d4 = *reinterpret_cast<const LDS f32x4 *>(vl + BN + r);
-                    const float lv[4] = {l4[0], l4[1], l4[2], l4[3]};
-                    const float dv4[4] = {d4[0], d4[1], d4[2], d4[3]};
-                    float pr[4], ds[4];
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const int i = u * BN + r + w;
-                        const bool ok = full || (i < S && kj < S && kj >= i - p.win_lo &&
-                                                 kj <= i + p.win_hi);
-                        pr[w] = ok ? __builtin_amdgcn_exp2f(fmaf(sa[4 * a + w], c2, -lv[w]))
-                                   : 0.0f;
-                        ds[w] = pr[w] * (da[4 * a + w] - dv4[w]);
-                    }
-                    pp[2 * a] = Elem<T>::pack(pr[0], pr[1]);
-                    pp[2 * a + 1] = Elem<T>::pack(pr[2], pr[3]);
-                    dsp[2 * a] = Elem<T>::pack(ds[0], ds[1]);
-                    dsp[2 * a + 1] = Elem<T>::pack(ds[2], ds[3]);
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        dva[db] = Elem<T>::mma(read_tr(dotr, o, db, 2 * sb + hh), half_of(pp, hh),
-                                               dva[db]);
-                        dka[db] = Elem<T>::mma(read_tr(qtr, o, db, 2 * sb + hh), half_of(dsp, hh),
-                                               dka[db]);
-                    }
+            for (int c = 0; c < NDC; ++c) {
+                sa = Elem<T>::mma(read_rows(qr, o, 0, c), kf[c], sa);
+                da = Elem<T>::mma(read_rows(dor, o, 0, c), read_rows(vw, o, 0, c), da);
             }
-            if (more && threadIdx.x < BN) put_vec(s ^ 1, nl2, ndr);
+            // element e: query u*QB + 8(e/4) + 4g + e%4, key kj
+            uint32_t pp[8], dsp[8];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int r = 8 * a + 4 * g;  // row of element 4a within the tile
+                const f32x4 l4 = *reinterpret_cast<const LDS f32x4 *>(vl + r);
+                const f32x4 d4 = *reinterpret_cast<const LDS f32x4 *>(vl + QB + r);
+                float pr[4], ds[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int i = u * QB + r + w;
+                    const bool ok =
+                        full || (i < S && kj < S && kj >= i - p.win_lo && kj <= i + p.win_hi);
+                    pr[w] = ok ? __builtin_amdgcn_exp2f(fmaf(sa[4 * a + w], c2, -l4[w])) : 0.0f;
+                    ds[w] = pr[w] * (da[4 * a + w] - d4[w]);
+                }
+                pp[2 * a] = Elem<T>::pack(pr[0], pr[1]);
+                pp[2 * a + 1] = Elem<T>::pack(pr[2], pr[3]);
+                dsp[2 * a] = Elem<T>::pack(ds[0], ds[1]);
+                dsp[2 * a + 1] = Elem<T>::pack(ds[2], ds[3]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dva[db] =
+                        Elem<T>::mma(read_tr(dotr, o, db, hh), half_of(pp, hh), dva[db]);
+                    dka[db] =
+                        Elem<T>::mma(read_tr(qtr, o, db, hh), half_of(dsp, hh), dka[db]);
+                }
+            if (more && threadIdx.x < QB) put_vec(s ^ 1, nl2, ndr);
         }
         if (kj < S) {
             store_rows(static_cast<uint16_t *>(p.dv) + head, kj, g, dva, 1.0f);
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(64 * kDqWaves, 1) void fa_bwd_dq_kernel(BwdParams p
 
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void fa_bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * Bwd<T, D>::kKvStage];
+    __shared__ __attribute__((aligned(1024))) char smem[Bwd<T, D>::kKvV + 2 * Bwd<T, D>::kKvStage];
     Bwd<T, D>::dkdv(p, (LDS char *)smem);
 }
 
