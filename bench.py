@@ -44,6 +44,58 @@ DECODE_SOURCES = ["tiled_attention_11_amd/csrc/fa_decode.hip",
                   "tiled_attention_11_amd/csrc/fa_device.h"]
 
 
+class ClockSampler:
+    """Samples the GPU shader clock (the active level of the DPM table in
+    sysfs) from a background thread while launches run; the median of the
+    samples above idle is the clock the kernels ran at. None where the file
+    is not readable."""
+
+    def __init__(self, period_s=0.003):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))[:1]
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            for p in self.paths:
+                try:
+                    for line in open(p).read().splitlines():
+                        m = re.search(r"(\d+)\s*Mhz\s*\*", line)
+                        if m:
+                            self.samples.append(int(m.group(1)))
+                except OSError:
+                    return
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def mhz(self):
+        busy = sorted(x for x in self.samples if x >= 1000)
+        return busy[len(busy) // 2] if busy else None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def kernel_sha256(sources=None):
     h = hashlib.sha256()
     for rel in sources or KERNEL_SOURCES:
@@ -118,7 +170,7 @@ def cpu_baseline(w, q, k, v, o_gpu, lse_gpu, seconds):
                  w["dtype"])
     base = {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": orc.max_threads(),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": cpu_model(),
         "sample": (f"{n} query rows drawn uniformly (seed 1234) from the same workload, "
                    f"{pairs} visible pairs, {dt:.2f} s wall, fp64"),
     }
@@ -584,6 +636,12 @@ def main():
     per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]) * 1e-3
     total_s = evs[0].elapsed_time(evs[-1]) * 1e-3
     avg_s = total_s / args.steps
+    # the shader clock under this load: sampled over half a second of the
+    # same launches, after (and outside) the timed region
+    with ClockSampler() as clk:
+        for _ in range(max(50, int(0.5 / avg_s))):
+            step()
+        torch.cuda.synchronize()
     print(f"[bench] timed {args.steps} steps: avg {avg_s * 1e6:.1f} us, median "
           f"{np.median(per) * 1e6:.1f} us, wall {t_wall:.3f} s", file=sys.stderr, flush=True)
 
@@ -626,6 +684,13 @@ def main():
         },
         "pct_of_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 2),
         "median_launch_us": round(float(np.median(per)) * 1e6, 2),
+        "min_launch_us": round(float(np.min(per)) * 1e6, 2),
+        "tflops_at_median": round(flops / float(np.median(per)) / 1e12, 2),
+        # the shader clock under this load (sysfs DPM level, sampled during the
+        # timed launches) and the dense fp16 MFMA peak at that clock
+        "sclk_mhz": clk.mhz(),
+        "pct_of_clock_adjusted_peak": (round(100.0 * tflops / (256 * 4096 * clk.mhz() * 1e-6), 2)
+                                       if clk.mhz() else None),
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
