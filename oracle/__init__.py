@@ -52,6 +52,10 @@ def _bind(lib):
         _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64, _i64,
         ctypes.c_int, _ptr, _ptr, ctypes.c_int, _i64, _ptr, _ptr, _ptr, ctypes.c_int]
     lib.oracle_attention_rope_rows.restype = ctypes.c_int
+    lib.oracle_attention_kv_rope.argtypes = [
+        _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64,
+        _i64, ctypes.c_int, _ptr, _ptr, ctypes.c_int, _ptr, _ptr, ctypes.c_int]
+    lib.oracle_attention_kv_rope.restype = ctypes.c_int
     lib.oracle_attention_bwd.argtypes = [
         _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _i64,
         _i64, ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, ctypes.c_int]
@@ -241,6 +245,30 @@ class Oracle:
         o, lse = self.attention_rope_rows(q, k, v, dtype, scale, mask, window, cos, sin, mode,
                                           None, nthreads)
         return o.reshape(B, H, S, D), lse.reshape(B, H, S)
+
+    def attention_kv_rope(self, q, k, v, dtype, scale, mask, window, cos, sin, mode,
+                          nthreads=0):
+        """:meth:`attention_kv` with the new query rows rotated (RoPE) at their
+        positions Sk - Sq + i and rounded to ``dtype``; the cache keys are used
+        as given (already rotated)."""
+        q = np.ascontiguousarray(q, dtype=np.uint16)
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        v = np.ascontiguousarray(v, dtype=np.uint16)
+        B, H, Sq, D = q.shape
+        Sk = k.shape[2]
+        cos, sin = self._tables(cos, sin, D)
+        if cos.shape[0] < Sk:
+            raise ValueError("the tables need a row per cached position")
+        m, wl, wr = self._mask_args(mask, window)
+        o = np.empty((B, H, Sq, D), dtype=np.float64)
+        lse = np.empty((B, H, Sq), dtype=np.float64)
+        rc = self.lib.oracle_attention_kv_rope(
+            q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Sq, Sk, D, float(scale), m, wl,
+            wr, _DTYPES[dtype], cos.ctypes.data, sin.ctypes.data, self._ROPE_MODES[mode],
+            o.ctypes.data, lse.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise ValueError("oracle_attention_kv_rope rejected its arguments")
+        return o, lse
 
     def attention_varlen(self, q, k, v, cu_seqlens, dtype, scale, mask, window=(-1, -1),
                          nthreads=0):

@@ -522,6 +522,58 @@ int oracle_attention_rope_rows(const uint16_t *q, const uint16_t *k, const uint1
     return failed ? -1 : 0;
 }
 
+/* New query rows against a key/value cache whose keys are already rotated
+ * (a rotary-embedding cache): query row i of a head is rotated by
+ * oracle_rope_rows at its position Sk - Sq + i and each value rounded to the
+ * element type (as in oracle_attention_rope_rows), then attends to the cached
+ * keys as given, under the rules of oracle_attention_kv. Reading: the
+ * tile-fusion page, section 9, rotates Q and K as their tiles load; keys
+ * enter the cache rotated, so only the new rows are rotated here.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_attention_kv_rope(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                             double scale, int mask_mode, int64_t wl, int64_t wr, int dtype,
+                             const float *cos_t, const float *sin_t, int mode, double *o,
+                             double *lse, int nthreads)
+{
+    if (check_args(B, H, Sk, D, mask_mode, dtype)) return -1;
+    if (Sq < 1 || Sq > Sk || D % 2 || (mode != 0 && mode != 1)) return -1;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    nthreads = 1;
+#endif
+    double *kd = (double *)malloc(sizeof(double) * (size_t)(Sk * D));
+    if (!kd) return -1;
+    int failed = 0;
+    for (int64_t bh = 0; bh < B * H && !failed; ++bh) {
+        for (int64_t t = 0; t < Sk * D; ++t) kd[t] = decode(k[bh * Sk * D + t], dtype);
+#pragma omp parallel num_threads(nthreads) reduction(| : failed)
+        {
+            double *srow = (double *)malloc(sizeof(double) * (size_t)Sk);
+            double *qrow = (double *)malloc(sizeof(double) * (size_t)D);
+            double *orow = (double *)malloc(sizeof(double) * (size_t)D);
+            if (!srow || !qrow || !orow) {
+                failed = 1;
+            } else {
+#pragma omp for schedule(static)
+                for (int64_t i = 0; i < Sq; ++i) {
+                    const int64_t r = bh * Sq + i, pos = Sk - Sq + i;
+                    oracle_rope_rows(q + r * D, 1, D, &pos, cos_t, sin_t, mode, dtype, qrow);
+                    for (int64_t d = 0; d < D; ++d) qrow[d] = oracle_round(qrow[d], dtype);
+                    one_row_f64(qrow, kd, v + bh * Sk * D, Sk, D, scale, mask_mode, wl, wr,
+                                dtype, pos, srow, orow, o + r * D, lse + r);
+                }
+            }
+            free(srow);
+            free(qrow);
+            free(orow);
+        }
+    }
+    free(kd);
+    return failed ? -1 : 0;
+}
+
 /* Gradients of the attention (the backward pass) for every head of
  * [B,H,S,D] inputs, given dO = dL/dO for some loss L.
  * The ops-transformer walkthrough (hwcomputing.csdn.net, 6a0ef689), closing

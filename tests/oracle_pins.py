@@ -567,6 +567,33 @@ def pin_bwd_closed_forms(orc):
     assert abs(lhs - rhs) < 1e-10 * (1 + abs(lhs))
 
 
+def pin_kv_rope_is_the_tail_of_the_square_case(orc):
+    """New rows against a cache of rotated keys give the last rows of the square
+    RoPE attention when the cache holds the square case's keys rotated and
+    rounded (numpy complex rotation, numpy float16 rounding); zero angles give
+    the plain cache attention."""
+    from synth import rope_tables
+    Sk, D = 40, 16
+    for mode in ("halves", "interleaved"):
+        Q, K, V = make_qkv(1, 2, Sk, D, "f16", seed=41)
+        cos, sin = rope_tables(Sk + 3, D, base=50.0)
+        krot = _rope_complex(_decode_ref(K, "f16"), np.arange(Sk), cos, sin, mode)
+        kbits = f32_to_bits(krot.astype(np.float16).astype(np.float32), "f16")
+        o_sq, lse_sq = orc.attention_rope(Q, K, V, "f16", 0.3, "causal", (-1, -1), cos, sin, mode)
+        for Sq in (1, 5, Sk):
+            q = np.ascontiguousarray(Q[:, :, Sk - Sq:, :])
+            o, lse = orc.attention_kv_rope(q, kbits, V, "f16", 0.3, "causal", (-1, -1), cos, sin,
+                                           mode)
+            assert np.max(np.abs(o - o_sq[:, :, Sk - Sq:, :])) < 1e-12, (mode, Sq)
+            assert np.max(np.abs(lse - lse_sq[:, :, Sk - Sq:])) < 1e-12, (mode, Sq)
+    q, k, v = make_qkv(1, 2, 7, D, "bf16", seed=42)
+    _, k2, v2 = make_qkv(1, 2, 30, D, "bf16", seed=43)
+    one, zero = np.ones((30, D // 2), np.float32), np.zeros((30, D // 2), np.float32)
+    o, lse = orc.attention_kv_rope(q, k2, v2, "bf16", 0.5, "window", (9, 0), one, zero, "halves")
+    o0, lse0 = orc.attention_kv(q, k2, v2, "bf16", 0.5, "window", (9, 0))
+    assert np.array_equal(o, o0) and np.array_equal(lse, lse0)
+
+
 def pin_kv_is_the_tail_of_the_square_case(orc):
     """New rows at the end of a sequence give the last rows of the square
     problem whose query rows end with them (any earlier query rows)."""
@@ -623,4 +650,5 @@ ALL_PINS = [
     pin_rope_zero_angle_is_plain_attention,
     pin_bwd_autograd,
     pin_bwd_closed_forms,
+    pin_kv_rope_is_the_tail_of_the_square_case,
 ]
