@@ -345,6 +345,35 @@ int64_t fa_decode_paged_workspace_bytes(int B, int H, int Sq, int max_seq_len, i
                                         int mask_mode, int win_l, int win_r);
 
 /*
+ * fa_decode_rope, fa_decode_paged_rope -- fa_decode and fa_decode_paged with
+ * the rotary embedding of the new query rows: row i (at position
+ * Sk - Sq + i, or seq_lens[b] - Sq + i for a paged sequence) turns as fa_rope
+ * turns row position, in fp32, and enters Q K^T rounded to `dtype`. The cache
+ * holds keys already rotated (as fa_fwd_rope's k_rot or fa_rope leave them),
+ * so they are read as given. Defining passage: the tile-fusion page, section 9
+ * (RoPE applied as the Q and K tiles load; keys are rotated once, when cached).
+ *
+ * cos_table, sin_table, n_pos, rope_mode  as for fa_rope, with n_pos >= Sk (or
+ * max_seq_len): positions past the tables' end never occur; a row at a
+ * negative position (a paged sequence shorter than Sq) uses row 0 and sees no
+ * key anyway. The tables must not overlap o, lse or the workspace.
+ * Every other argument, the workspace (same size as without RoPE) and the
+ * error rules as fa_decode / fa_decode_paged.
+ */
+int fa_decode_rope(const void *q, const void *k, const void *v, void *o, float *lse,
+                   const float *cos_table, const float *sin_table, int n_pos, int rope_mode,
+                   int B, int H, int Sq, int Sk, int D, float scale, int mask_mode, int win_l,
+                   int win_r, int dtype, void *workspace, int64_t workspace_bytes,
+                   hipStream_t stream);
+int fa_decode_paged_rope(const void *q, const void *k_pages, const void *v_pages, void *o,
+                         float *lse, const int32_t *block_table, const int32_t *seq_lens,
+                         const float *cos_table, const float *sin_table, int n_pos,
+                         int rope_mode, int B, int H, int Sq, int max_seq_len, int D,
+                         int num_pages, int page_size, int max_pages, float scale,
+                         int mask_mode, int win_l, int win_r, int dtype, void *workspace,
+                         int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * fa_decode_flops -- algorithmic FLOPs of one fa_decode call: 4 * D * B * H *
  * (visible (row, key) pairs), rows at positions Sk - Sq .. Sk - 1. Returns the
  * count, or a negative fa_status.

@@ -169,3 +169,69 @@ def test_named_workload_sampled_rows(orc):
     st = compare(to_bits(o).reshape(-1, D)[rows], lse.cpu().numpy().reshape(-1)[rows], o_ref,
                  lse_ref, "f16")
     assert st["pass"], st
+
+
+# ---------------------------------------------------------------------------
+# new rows against a cache of rotated keys
+
+DEC_SHAPES = [(2, 3, 1, 777, 128), (1, 2, 16, 2000, 64), (2, 2, 5, 129, 128), (1, 4, 32, 32, 64)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", DEC_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("mode", ["halves", "interleaved"])
+@pytest.mark.parametrize("mask,window", [("causal", (-1, -1)), ("window", (100, 0))], ids=str)
+def test_decode_rope_parity(orc, dtype, shape, mode, mask, window):
+    B, H, Sq, Sk, D = shape
+    seed = 720 + Sq + Sk + D
+    say("decode_rope", dtype, shape, mode, mask, window, "seed", seed)
+    q, _, _ = synth.make_qkv(B, H, Sq, D, dtype, seed)
+    _, k, v = synth.make_qkv(B, H, Sk, D, dtype, seed + 1)
+    cos, sin, tc, ts = tables(Sk + 9, D)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = fa.decode(to_device(q, dtype), to_device(k, dtype), to_device(v, dtype), scale=scale,
+                       mask=mask, window=window, rope=(tc, ts, mode))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.attention_kv_rope(q, k, v, dtype, scale, mask, window, cos, sin, mode)
+    st = compare(to_bits(o), lse.cpu().numpy(), o_ref, lse_ref, dtype)
+    assert st["pass"], st
+
+
+def test_decode_rope_continues_the_prefill(orc):
+    """A prefill with fa_fwd_rope fills the cache (k_rot); the cache call with
+    the new rows rotated at the end positions reproduces the prefill's last
+    rows (fp16, causal)."""
+    B, H, S, D, Sq = 1, 3, 600, 128, 8
+    say("decode_rope after prefill", (B, H, S, D, Sq))
+    q, k, v = synth.make_qkv(B, H, S, D, "f16", seed=730)
+    cos, sin, tc, ts = tables(S, D)
+    tq, tk, tv = (to_device(x, "f16") for x in (q, k, v))
+    o_full, lse_full, k_rot = fa.forward_rope(tq, tk, tv, tc, ts, mask="causal")
+    o_dec, lse_dec = fa.decode(tq[:, :, S - Sq:].contiguous(), k_rot, tv, mask="causal",
+                               rope=(tc, ts, "halves"))
+    torch.cuda.synchronize()
+    # both are within tolerance of the same oracle rows; compare them directly
+    a = decode(to_bits(o_dec), "f16")
+    b = decode(to_bits(o_full[:, :, S - Sq:]), "f16")
+    assert np.max(np.abs(a - b)) <= 2e-3
+    assert np.max(np.abs(lse_dec.cpu().numpy() - lse_full[:, :, S - Sq:].cpu().numpy())) <= 1e-3
+
+
+def test_decode_paged_rope_parity(orc):
+    """The paged cache with rotated new rows, against the oracle on the same
+    (contiguous) cache."""
+    B, H, Sq, Sk, D, ps = 2, 4, 3, 1024, 128, 64
+    say("decode_paged_rope", (B, H, Sq, Sk, D, ps))
+    q, _, _ = synth.make_qkv(B, H, Sq, D, "f16", seed=731)
+    _, k, v = synth.make_qkv(B, H, Sk, D, "f16", seed=732)
+    kp, vp, table = synth.paged_cache(k, v, ps, seed=733)
+    cos, sin, tc, ts = tables(Sk, D)
+    lens = torch.full((B,), Sk, dtype=torch.int32, device="cuda")
+    o, lse = fa.decode_paged(to_device(q, "f16"), to_device(kp, "f16"), to_device(vp, "f16"),
+                             torch.from_numpy(table).cuda(), lens, Sk, mask="causal",
+                             rope=(tc, ts, "interleaved"))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.attention_kv_rope(q, k, v, "f16", 1.0 / math.sqrt(D), "causal",
+                                           (-1, -1), cos, sin, "interleaved")
+    st = compare(to_bits(o), lse.cpu().numpy(), o_ref, lse_ref, "f16")
+    assert st["pass"], st

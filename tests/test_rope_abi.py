@@ -56,3 +56,24 @@ def test_fwd_rope_in_place_and_empty_are_accepted_on_the_host():
     # B*H*S == 0 returns before any launch; an in-place k_rot passes the checks
     assert fwd(B=0, kr=K) == OK
     assert fwd(S=0, n_pos=0) == OK
+
+
+def dec(rope_mode=0, n_pos=100, c=C, Sq=4, Sk=100, o=O):
+    return fa.fa_decode_rope(Q, K, V, o, L, c, S_, n_pos, rope_mode, 2, 3, Sq, Sk, 128, 0.1, 1,
+                             -1, -1, 0, DQ_WS, 1 << 30, None)
+
+
+DQ_WS = 11 * 4 * GB
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rope_mode=3), INVALID), (dict(n_pos=99), INVALID), (dict(c=None), INVALID),
+    (dict(c=C + 4), ALIGN), (dict(c=O + 64), INVALID), (dict(Sq=40), UNSUPPORTED),
+])
+def test_decode_rope_rejected_before_launch(kw, code):
+    assert dec(**kw) == code
+
+
+def test_decode_paged_rope_rejects_page_size_zero():
+    assert fa.fa_decode_paged_rope(Q, K, V, O, L, X, Y, C, S_, 100, 0, 2, 3, 1, 100, 128, 8, 0, 2,
+                                   0.1, 1, -1, -1, 0, DQ_WS, 1 << 30, None) == UNSUPPORTED

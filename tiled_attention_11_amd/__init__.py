@@ -3,7 +3,8 @@
 A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
 ``fa_fwd``, ``fa_visible_pairs``, ``fa_fwd_flops``, ``fa_fwd_varlen``,
 ``fa_fwd_varlen_flops``, ``fa_rope``, ``fa_fwd_rope``, ``fa_bwd``,
-``fa_bwd_workspace_bytes``, ``fa_bwd_flops``, ``fa_decode``,
+``fa_bwd_workspace_bytes``, ``fa_bwd_flops``, ``fa_decode``, ``fa_decode_rope``,
+``fa_decode_paged_rope``,
 ``fa_decode_workspace_bytes``, ``fa_decode_flops``, ``fa_decode_paged``,
 ``fa_decode_paged_workspace_bytes`` and ``fa_strerror`` carry the C names and
 arguments (marshalling only). ``forward``, ``forward_varlen``, ``rope``,
@@ -21,7 +22,8 @@ __all__ = [
     "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
     "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
     "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_rope", "fa_fwd_rope", "FA_ROPE_HALVES",
-    "FA_ROPE_INTERLEAVED", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_flops", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
+    "FA_ROPE_INTERLEAVED", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_flops", "fa_decode",
+    "fa_decode_rope", "fa_decode_paged_rope", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
     "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "forward_varlen", "rope", "forward_rope", "backward", "decode",
     "decode_paged",
     "lib_path", "library",
@@ -80,6 +82,13 @@ def _load():
     lib.fa_bwd_workspace_bytes.restype = i64
     lib.fa_bwd_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     lib.fa_bwd_flops.restype = i64
+    lib.fa_decode_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci,
+                                   ctypes.c_float, ci, ci, ci, ci, vp, i64, vp]
+    lib.fa_decode_rope.restype = ci
+    lib.fa_decode_paged_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
+                                         ci, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci, ci, vp,
+                                         i64, vp]
+    lib.fa_decode_paged_rope.restype = ci
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci,
                               ci, ci, vp, i64, vp]
     lib.fa_decode.restype = ci
@@ -175,6 +184,26 @@ def fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, 
     """Call ``fa_decode`` with raw device addresses (ints); return its status."""
     return _lib.fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r,
                           dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_rope(q, k, v, o, lse, cos_table, sin_table, n_pos, rope_mode, B, H, Sq, Sk, D,
+                   scale, mask_mode, win_l, win_r, dtype, workspace, workspace_bytes, stream):
+    """Call ``fa_decode_rope`` with raw device addresses (ints); return its status."""
+    return _lib.fa_decode_rope(q, k, v, o, lse, cos_table, sin_table, n_pos, rope_mode, B, H, Sq,
+                               Sk, D, scale, mask_mode, win_l, win_r, dtype, workspace,
+                               workspace_bytes, stream)
+
+
+def fa_decode_paged_rope(q, k_pages, v_pages, o, lse, block_table, seq_lens, cos_table,
+                         sin_table, n_pos, rope_mode, B, H, Sq, max_seq_len, D, num_pages,
+                         page_size, max_pages, scale, mask_mode, win_l, win_r, dtype, workspace,
+                         workspace_bytes, stream):
+    """Call ``fa_decode_paged_rope`` with raw device addresses (ints); return its status."""
+    return _lib.fa_decode_paged_rope(q, k_pages, v_pages, o, lse, block_table, seq_lens,
+                                     cos_table, sin_table, n_pos, rope_mode, B, H, Sq,
+                                     max_seq_len, D, num_pages, page_size, max_pages, scale,
+                                     mask_mode, win_l, win_r, dtype, workspace, workspace_bytes,
+                                     stream)
 
 
 def fa_decode_workspace_bytes(B, H, Sq, Sk, D, mask_mode, win_l=-1, win_r=-1):
@@ -458,7 +487,7 @@ def backward(q, k, v, o, lse, dout, *, scale=None, mask="full", window=(-1, -1),
 
 
 def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse=None,
-           return_lse=True, workspace=None, stream=None):
+           return_lse=True, workspace=None, rope=None, stream=None):
     """New query rows against a key/value cache on torch device tensors.
 
     q: contiguous [B, H, Sq, D] (Sq <= 32); k, v: contiguous [B, H, Sk, D]
@@ -466,7 +495,9 @@ def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse
     position Sk - Sq + i; ``mask``/``window`` as for ``forward``, applied at
     that position. ``workspace``: optional uint8 device tensor of at least
     ``fa_decode_workspace_bytes(...)`` bytes (allocated here when needed and
-    not given). Returns ``(o, lse)``.
+    not given). ``rope``: optional ``(cos, sin, mode)`` (float32 [n_pos, D/2]
+    tables, "halves" or "interleaved") to rotate the new rows at their
+    positions; the cache holds rotated keys. Returns ``(o, lse)``.
     """
     import torch
 
@@ -507,18 +538,27 @@ def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
-        status = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           lse.data_ptr() if lse is not None else None, B, H, Sq, Sk, D,
-                           float(scale), m, int(wl), int(wr), dtype, ws_ptr, int(ws_bytes),
-                           stream)
+        if rope is None:
+            status = fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr() if lse is not None else None, B, H, Sq, Sk, D,
+                               float(scale), m, int(wl), int(wr), dtype, ws_ptr, int(ws_bytes),
+                               stream)
+        else:
+            cos, sin, mode = rope
+            _check_tables(cos, sin, D, q)
+            status = fa_decode_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, cos.data_ptr(),
+                                    sin.data_ptr(), cos.shape[0], _rope_code(mode), B, H, Sq,
+                                    Sk, D, float(scale), m, int(wl), int(wr), dtype, ws_ptr,
+                                    int(ws_bytes), stream)
     if status != 0:
-        raise FaError(status, "fa_decode")
+        raise FaError(status, "fa_decode" if rope is None else "fa_decode_rope")
     return out, lse
 
 
 def decode_paged(q, k_pages, v_pages, block_table, seq_lens, max_seq_len, *, scale=None,
                  mask="causal", window=(-1, -1), out=None, lse=None, return_lse=True,
-                 workspace=None, stream=None):
+                 workspace=None, rope=None, stream=None):
     """``decode`` over a paged cache on torch device tensors.
 
     q: contiguous [B, H, Sq, D]; k_pages, v_pages: contiguous
@@ -565,12 +605,22 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, max_seq_len, *, sca
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
-        status = fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
-                                 out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                                 block_table.data_ptr(), seq_lens.data_ptr(), B, H, Sq,
-                                 int(max_seq_len), D, num_pages, page_size, max_pages,
-                                 float(scale), m, int(wl), int(wr), dtype, ws_ptr, int(ws_bytes),
-                                 stream)
+        if rope is None:
+            status = fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                     out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                     block_table.data_ptr(), seq_lens.data_ptr(), B, H, Sq,
+                                     int(max_seq_len), D, num_pages, page_size, max_pages,
+                                     float(scale), m, int(wl), int(wr), dtype, ws_ptr,
+                                     int(ws_bytes), stream)
+        else:
+            cos, sin, mode = rope
+            _check_tables(cos, sin, D, q)
+            status = fa_decode_paged_rope(
+                q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), out.data_ptr(),
+                lse.data_ptr() if lse is not None else None, block_table.data_ptr(),
+                seq_lens.data_ptr(), cos.data_ptr(), sin.data_ptr(), cos.shape[0],
+                _rope_code(mode), B, H, Sq, int(max_seq_len), D, num_pages, page_size, max_pages,
+                float(scale), m, int(wl), int(wr), dtype, ws_ptr, int(ws_bytes), stream)
     if status != 0:
-        raise FaError(status, "fa_decode_paged")
+        raise FaError(status, "fa_decode_paged" if rope is None else "fa_decode_paged_rope")
     return out, lse

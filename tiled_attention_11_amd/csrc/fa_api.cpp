@@ -566,7 +566,7 @@ int decode_common(const void *q, const void *k, const void *v, void *o, float *l
                   int Sq, int Sk, int D, float scale, int mask_mode, int win_l, int win_r,
                   int dtype, void *workspace, int64_t workspace_bytes, hipStream_t stream,
                   const int32_t *block_table, const int32_t *seq_lens, int num_pages,
-                  int page_size, int max_pages) {
+                  int page_size, int max_pages, const RopeArgs *rope = nullptr) {
     // ---- scalar arguments and the plan (no HIP work queued before success) ----
     if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return FA_ERR_INVALID_ARG;
@@ -578,6 +578,22 @@ int decode_common(const void *q, const void *k, const void *v, void *o, float *l
         if ((int64_t)B * max_pages > (int64_t)INT32_MAX) return FA_ERR_TOO_LARGE;
         // one page's rows of one head must stay inside a 32-bit buffer range
         if ((uint64_t)page_size * H * D * 2 >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    }
+    if (rope) {
+        // tables [n_pos >= Sk, D/2] fp32, 16-byte aligned, clear of o and lse
+        // (checked before the plan, which queries the device)
+        if (rope->mode != FA_ROPE_HALVES && rope->mode != FA_ROPE_INTERLEAVED)
+            return FA_ERR_INVALID_ARG;
+        if (!rope->cos || !rope->sin || rope->n_pos < Sk) return FA_ERR_INVALID_ARG;
+        if (((uintptr_t)rope->cos | (uintptr_t)rope->sin) & 15u) return FA_ERR_ALIGNMENT;
+        if (B >= 0 && H >= 0 && Sq >= 0 && (D == 64 || D == 128)) {
+            const uint64_t tbytes = (uint64_t)rope->n_pos * (D / 2) * 4;
+            const uint64_t ob = (uint64_t)B * H * Sq * D * 2, lb = (uint64_t)B * H * Sq * 4;
+            for (const void *t : {(const void *)rope->cos, (const void *)rope->sin})
+                if (overlaps((uintptr_t)o, ob, (uintptr_t)t, tbytes) ||
+                    (lse && overlaps((uintptr_t)lse, lb, (uintptr_t)t, tbytes)))
+                    return FA_ERR_INVALID_ARG;
+        }
     }
     DecodePlan pl;
     const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, paged, &pl);
@@ -612,6 +628,12 @@ int decode_common(const void *q, const void *k, const void *v, void *o, float *l
         for (int b = a + 1; b < 3; ++b)
             if (outn[b] && overlaps(outs[a], outn[a], outs[b], outn[b])) return FA_ERR_INVALID_ARG;
     }
+    if (rope) {  // the workspace must not overlap the tables either
+        const uint64_t tbytes = (uint64_t)rope->n_pos * (D / 2) * 4;
+        if (wbytes && (overlaps(pw, wbytes, (uintptr_t)rope->cos, tbytes) ||
+                       overlaps(pw, wbytes, (uintptr_t)rope->sin, tbytes)))
+            return FA_ERR_INVALID_ARG;
+    }
 
     // ---- launch -------------------------------------------------------------------
     fa::DecodeParams p;
@@ -637,6 +659,9 @@ int decode_common(const void *q, const void *k, const void *v, void *o, float *l
     p.page_size = paged ? page_size : 0;
     p.max_pages = paged ? max_pages : 0;
     p.num_pages = paged ? num_pages : 0;
+    p.rope_cos = rope ? rope->cos : nullptr;
+    p.rope_sin = rope ? rope->sin : nullptr;
+    p.rope_interleaved = rope ? rope->mode == FA_ROPE_INTERLEAVED : 0;
     hipError_t err = fa::launch_decode(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -661,4 +686,29 @@ extern "C" int fa_decode_paged(const void *q, const void *k_pages, const void *v
     return decode_common(q, k_pages, v_pages, o, lse, B, H, Sq, max_seq_len, D, scale, mask_mode,
                          win_l, win_r, dtype, workspace, workspace_bytes, stream, block_table,
                          seq_lens, num_pages, page_size, max_pages);
+}
+
+extern "C" int fa_decode_rope(const void *q, const void *k, const void *v, void *o, float *lse,
+                              const float *cos_table, const float *sin_table, int n_pos,
+                              int rope_mode, int B, int H, int Sq, int Sk, int D, float scale,
+                              int mask_mode, int win_l, int win_r, int dtype, void *workspace,
+                              int64_t workspace_bytes, hipStream_t stream) {
+    RopeArgs r{nullptr, nullptr, cos_table, sin_table, n_pos, rope_mode};
+    return decode_common(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
+                         workspace, workspace_bytes, stream, nullptr, nullptr, 0, 0, 0, &r);
+}
+
+extern "C" int fa_decode_paged_rope(const void *q, const void *k_pages, const void *v_pages,
+                                    void *o, float *lse, const int32_t *block_table,
+                                    const int32_t *seq_lens, const float *cos_table,
+                                    const float *sin_table, int n_pos, int rope_mode, int B,
+                                    int H, int Sq, int max_seq_len, int D, int num_pages,
+                                    int page_size, int max_pages, float scale, int mask_mode,
+                                    int win_l, int win_r, int dtype, void *workspace,
+                                    int64_t workspace_bytes, hipStream_t stream) {
+    if (page_size == 0) return FA_ERR_UNSUPPORTED;  // 0 would mean "not paged"
+    RopeArgs r{nullptr, nullptr, cos_table, sin_table, n_pos, rope_mode};
+    return decode_common(q, k_pages, v_pages, o, lse, B, H, Sq, max_seq_len, D, scale, mask_mode,
+                         win_l, win_r, dtype, workspace, workspace_bytes, stream, block_table,
+                         seq_lens, num_pages, page_size, max_pages, &r);
 }

@@ -187,6 +187,11 @@ struct Decode {
                 x ^= flip;
                 qf[c] = __builtin_bit_cast(vec8, x);
             }
+            if (p.rope_cos) {  // rotary embedding of the row at its position
+                const int64_t at = (int64_t)min(max(pos_first + l32, 0), p.Sk - 1) * (D / 2);
+                rope_fragments<T, D>(qf, g, p.rope_cos + at, p.rope_sin + at,
+                                     p.rope_interleaved != 0);
+            }
         }
 
         f32x16 oacc[NDB];

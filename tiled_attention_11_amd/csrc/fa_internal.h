@@ -117,6 +117,11 @@ struct DecodeParams {
     const int32_t *block_table;
     const int32_t *seq_lens;
     int page_size, max_pages, num_pages;
+    // Rotary embedding of the query rows (rope_cos == nullptr: none): row i
+    // turns by the angles of its position (table row, clamped into [0, Sk - 1]);
+    // the cache holds keys already rotated.
+    const float *rope_cos, *rope_sin;
+    int rope_interleaved;
 };
 
 // Enqueue the cache kernel (and, for nsplit > 1, the merge kernel).
