@@ -425,6 +425,32 @@ def _rope_complex(xd, pos, cos, sin, mode):
     return out
 
 
+def pin_pure_python(orc):
+    """The oracle against a per-element pure-Python evaluation of the
+    definition (math.fsum for every sum, math.exp, Python floats decoded by
+    numpy) on tiny shapes, every mask: within 1e-12."""
+    rng = np.random.default_rng(44)
+    for dtype in ("f16", "bf16"):
+        for S, D in ((1, 4), (5, 8), (12, 3)):
+            q, k, v = make_qkv(1, 2, S, D, dtype, seed=int(rng.integers(1 << 30)))
+            qd, kd, vd = (_decode_ref(x, dtype) for x in (q, k, v))
+            for mask, window in MASK_CASES:
+                vis = _bool_mask_kv(S, S, mask, window)
+                o, lse = orc.attention(q, k, v, dtype, 0.3, mask, window)
+                for h in range(2):
+                    for i in range(S):
+                        js = [j for j in range(S) if vis[i, j]]
+                        sc = {j: 0.3 * math.fsum(float(qd[0, h, i, d]) * float(kd[0, h, j, d])
+                                                 for d in range(D)) for j in js}
+                        m = max(sc.values())
+                        e = {j: math.exp(sc[j] - m) for j in js}
+                        den = math.fsum(e.values())
+                        for d in range(D):
+                            ref = math.fsum(e[j] * float(vd[0, h, j, d]) for j in js) / den
+                            assert abs(o[0, h, i, d] - ref) <= 1e-12 * max(1.0, abs(ref))
+                        assert abs(lse[0, h, i] - (m + math.log(den))) <= 1e-12 * max(1.0, abs(m))
+
+
 def pin_rope_is_complex_rotation(orc):
     """RoPE of a row equals multiplying each of its pairs, read as a complex
     number, by cos + i sin of the row's position (random angles), in both
@@ -644,6 +670,7 @@ ALL_PINS = [
     pin_kv_is_the_tail_of_the_square_case,
     pin_kv_uniform_weights,
     pin_varlen_block_diagonal_sdpa,
+    pin_pure_python,
     pin_round_to_element_type,
     pin_rope_is_complex_rotation,
     pin_rope_attention_sdpa,
