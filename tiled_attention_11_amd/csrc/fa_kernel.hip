@@ -344,49 +344,6 @@ struct Kernel {
     // group 0. K(t) is read in phases 2t and 2t + 1, V(t) in 2t + 2 and 2t + 3;
     // both stream in (DMA) two phases ahead and are double-buffered.
 
-    // O^T += V^T P^T for tile `vs`: chunk c's B operand is P^T elements
-    // 8(c%2) .. +7 of score block c/2 (keys 16c + 8a + 4g + b for element
-    // 4a + b); the A operand comes from two transposing reads, rows
-    // 16c + 4g + (0..3) and 16c + 8 + 4g + (0..3). Both row offsets are
-    // multiples of 4, which keeps the V swizzle of the lane's base row.
-    static __device__ __forceinline__ void pv(State &st, const uint32_t (&pk)[NKB][8],
-                                              const LDS char *vs, const Addr &ad) {
-#pragma unroll
-        for (int c = 0; c < NPC; ++c) {
-            const int kb = c >> 1, hh = c & 1;
-            const u32x4 pw = {pk[kb][4 * hh + 0], pk[kb][4 * hh + 1], pk[kb][4 * hh + 2],
-                              pk[kb][4 * hh + 3]};
-            const vec8 b = __builtin_bit_cast(vec8, pw);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const LDS char *base = vs + ad.v[db] + 16 * c * G::RB;
-                const fp16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base));
-                const fp16x4_t hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base + 8 * G::RB));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                const vec8 a = __builtin_bit_cast(vec8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-                st.oacc[db] = Elem<T>::mma(a, b, st.oacc[db]);
-            }
-        }
-    }
-
-    // S^T = K Q^T for tile `ks`. Score blocks are 32 rows apart and 32 is a
-    // multiple of the K swizzle period, so block 0's offsets serve every block.
-    static __device__ __forceinline__ void qk(f32x16 (&sacc)[NKB], const State &st,
-                                              const LDS char *ks, const Addr &ad) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < NDC; ++c) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const vec8 a = *reinterpret_cast<const LDS vec8 *>(ks + ad.k[c] + kb * 32 * G::RB);
-                sacc[kb] = Elem<T>::mma(a, st.qf[c], sacc[kb]);
-            }
-        }
-    }
-
     // Softmax of one tile: mask (boundary tiles), tile maximum, rescale of O
     // and l when some row's maximum outgrows the slack (always on the first
     // visible tile, where m_run is -inf), and the probabilities: rounded once
@@ -522,7 +479,11 @@ struct Kernel {
         // M_i: O takes the rescale the softmax of tile i - 1 asked for (a wave-
         // uniform branch, rarely taken once the row maxima settle), then
         // O^T += V^T P^T of tile i - 1 and S^T = K Q^T of tile i, as one stream
-        // of MFMAs whose LDS operands are read kDist MFMAs ahead.
+        // of MFMAs whose LDS operands are read kDist MFMAs ahead. P V chunk c's
+        // B operand is P^T elements 8(c%2) .. +7 of score block c/2 (keys
+        // 16c + 8a + 4g + b for element 4a + b); its A operand comes from two
+        // transposing reads, rows 16c + 4g + (0..3) and 16c + 8 + 4g + (0..3),
+        // offsets that keep the V swizzle of the lane's base row.
         template <bool QK, bool PV>
         __device__ __forceinline__ void mphase(State &st, f32x16 (&sacc)[NKB],
                                                const uint32_t (&pk)[NKB][8], int i) const {
