@@ -178,8 +178,14 @@ struct Bwd {
         const int S = p.S;
         constexpr int ROWS = 32 * kDqWaves;
         const int ntq = (S + ROWS - 1) / ROWS;
-        const int bh = (int)blockIdx.x / ntq;
-        const int qt = ntq - 1 - ((int)blockIdx.x - bh * ntq);  // longest rows first
+        // Heaviest first over the whole grid (under causal masks the last
+        // query rows see the most keys): every head's tile qt, then tile
+        // qt - 1, ... With B*H a multiple of 8, all tiles of a head land on
+        // one XCD (consecutive workgroups go to consecutive XCDs) and share
+        // its L2.
+        const int BH = p.B * p.H;
+        const int bh = (int)blockIdx.x % BH;
+        const int qt = ntq - 1 - (int)blockIdx.x / BH;
         const int q0 = qt * ROWS, qi = q0 + 32 * wave + l32;
         const int64_t head = (int64_t)bh * S * D;
         const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
@@ -274,9 +280,11 @@ struct Bwd {
         const int l32 = lane & 31, g = lane >> 5;
         const int S = p.S;
         constexpr int ROWS = 32 * kKvWaves;
-        const int ntk = (S + ROWS - 1) / ROWS;
-        const int bh = (int)blockIdx.x / ntk;
-        const int kt = (int)blockIdx.x - bh * ntk;  // under causal masks the first keys see most rows
+        // Heaviest first over the whole grid, as in dq (under causal masks
+        // the first keys see the most rows).
+        const int BH = p.B * p.H;
+        const int bh = (int)blockIdx.x % BH;
+        const int kt = (int)blockIdx.x / BH;
         const int k0 = kt * ROWS, kj = k0 + 32 * wave + l32;
         const int64_t head = (int64_t)bh * S * D;
         const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
