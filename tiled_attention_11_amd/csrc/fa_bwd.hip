@@ -238,20 +238,26 @@ struct Bwd {
                     sa = Elem<T>::mma(read_rows(kr, o, sb, c), qf[c], sa);
                     da = Elem<T>::mma(read_rows(vr, o, sb, c), df[c], da);
                 }
-                // element e: key t*BN + 32sb + 8(e/4) + 4g + e%4, query qi
+                // element e: key t*BN + 32sb + 8(e/4) + 4g + e%4, query qi. A hidden
+                // pair's exponent becomes -inf (exp2 gives exactly 0), by selects
+                // under one uniform branch, so no exponential sits behind a branch.
+                float x[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) x[e] = fmaf(sa[e], c2, -lse2);
+                if (!full) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = t * BN + 32 * sb + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const bool ok = j < S && j >= qi - p.win_lo && j <= qi + p.win_hi;
+                        x[e] = ok ? x[e] : -INFINITY;
+                    }
+                }
                 uint32_t dsp[8];
 #pragma unroll
                 for (int e = 0; e < 16; e += 2) {
-                    float ds[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int j = t * BN + 32 * sb + 8 * ((e + u) >> 2) + 4 * g + ((e + u) & 3);
-                        const bool ok = full || (j < S && j >= qi - p.win_lo && j <= qi + p.win_hi);
-                        const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(sa[e + u], c2, -lse2))
-                                            : 0.0f;
-                        ds[u] = pr * (da[e + u] - drow);
-                    }
-                    dsp[e >> 1] = Elem<T>::pack(ds[0], ds[1]);
+                    const float d0 = __builtin_amdgcn_exp2f(x[e]) * (da[e] - drow);
+                    const float d1 = __builtin_amdgcn_exp2f(x[e + 1]) * (da[e + 1] - drow);
+                    dsp[e >> 1] = Elem<T>::pack(d0, d1);
                 }
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
@@ -364,20 +370,31 @@ struct Bwd {
                 sa = Elem<T>::mma(read_rows(qr, o, 0, c), kf[c], sa);
                 da = Elem<T>::mma(read_rows(dor, o, 0, c), read_rows(vw, o, 0, c), da);
             }
-            // element e: query u*QB + 8(e/4) + 4g + e%4, key kj
+            // element e: query u*QB + 8(e/4) + 4g + e%4, key kj. Hidden pairs:
+            // exponent -inf by selects under one uniform branch, as in dq.
+            float x[16];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 l4 = *reinterpret_cast<const LDS f32x4 *>(vl + 8 * a + 4 * g);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) x[4 * a + w] = fmaf(sa[4 * a + w], c2, -l4[w]);
+            }
+            if (!full) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int i = u * QB + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const bool ok = i < S && kj < S && kj >= i - p.win_lo && kj <= i + p.win_hi;
+                    x[e] = ok ? x[e] : -INFINITY;
+                }
+            }
             uint32_t pp[8], dsp[8];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const int r = 8 * a + 4 * g;  // row of element 4a within the tile
-                const f32x4 l4 = *reinterpret_cast<const LDS f32x4 *>(vl + r);
-                const f32x4 d4 = *reinterpret_cast<const LDS f32x4 *>(vl + QB + r);
+                const f32x4 d4 = *reinterpret_cast<const LDS f32x4 *>(vl + QB + 8 * a + 4 * g);
                 float pr[4], ds[4];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    const int i = u * QB + r + w;
-                    const bool ok =
-                        full || (i < S && kj < S && kj >= i - p.win_lo && kj <= i + p.win_hi);
-                    pr[w] = ok ? __builtin_amdgcn_exp2f(fmaf(sa[4 * a + w], c2, -l4[w])) : 0.0f;
+                    pr[w] = __builtin_amdgcn_exp2f(x[4 * a + w]);
                     ds[w] = pr[w] * (da[4 * a + w] - d4[w]);
                 }
                 pp[2 * a] = Elem<T>::pack(pr[0], pr[1]);
