@@ -203,9 +203,8 @@ struct Bwd {
         const int qlast = min(q0 + ROWS - 1, S - 1);
         const int t_first = max(0, q0 - p.win_lo) / BN;
         const int t_last = min(S - 1, qlast + p.win_hi) / BN;
-        // tiles visible in full from every row of the workgroup
-        const int t_in_lo = (max(0, qlast - p.win_lo) + BN - 1) / BN;
-        const int t_in_hi = (min(S - 1, q0 + p.win_hi) + 1) / BN;
+        // the wave's rows (uniform): 32-key blocks are classified per wave
+        const int qw0 = q0 + 32 * wave, qw1 = min(qw0 + 31, S - 1);
 
         Offs o;
         make_offs(o, lane);
@@ -229,9 +228,16 @@ struct Bwd {
             const LDS char *kr = smem + s * kDqStage;
             const LDS char *kt = kr + G::TILE_BYTES;
             const LDS char *vr = kr + 2 * G::TILE_BYTES;
-            const bool full = t >= t_in_lo && t < t_in_hi && (t + 1) * BN <= S;
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
+                // Per wave (uniform): a key block that none of the wave's rows
+                // sees is skipped; one that all of them see in full is not masked.
+                const int kb0 = t * BN + 32 * sb, kb1 = min(kb0 + 31, S - 1);
+                const bool empty =
+                    qw0 >= S || kb0 >= S || kb0 > qw1 + p.win_hi || kb1 < qw0 - p.win_lo;
+                if (empty) continue;
+                const bool full = qw0 + 32 <= S && kb0 + 32 <= S && kb0 >= qw0 + 31 - p.win_lo &&
+                                  kb0 + 31 <= qw0 + p.win_hi;
                 f32x16 sa = f32x16{}, da = f32x16{};
 #pragma unroll
                 for (int c = 0; c < NDC; ++c) {
@@ -329,7 +335,7 @@ struct Bwd {
         auto fetch_vec = [&](int u, float &l2, float &dr) {
             const int i = u * QB + (int)threadIdx.x;
             l2 = i < S ? lse_h[i] * kLog2e : 0.0f;
-            dr = i < S ? dot_h[i] : 0.0f;
+            dr = i < S ? -dot_h[i] : 0.0f;
         };
         auto put_vec = [&](int s, float l2, float dr) {
             LDS float *v =
@@ -364,7 +370,13 @@ struct Bwd {
             const LDS char *dotr = qr + 3 * GQ::TILE_BYTES;
             const LDS float *vl = reinterpret_cast<const LDS float *>(qr + 4 * GQ::TILE_BYTES);
             const bool full = u >= u_in_lo && u < u_in_hi && (u + 1) * QB <= S && keys_in;
-            f32x16 sa = f32x16{}, da = f32x16{};
+            f32x16 sa = f32x16{}, da;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const f32x4 d4 = *reinterpret_cast<const LDS f32x4 *>(vl + QB + 8 * a + 4 * g);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) da[4 * a + w] = d4[w];
+            }
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
                 sa = Elem<T>::mma(read_rows(qr, o, 0, c), kf[c], sa);
@@ -390,12 +402,11 @@ struct Bwd {
             uint32_t pp[8], dsp[8];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const f32x4 d4 = *reinterpret_cast<const LDS f32x4 *>(vl + QB + 8 * a + 4 * g);
                 float pr[4], ds[4];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     pr[w] = __builtin_amdgcn_exp2f(x[4 * a + w]);
-                    ds[w] = pr[w] * (da[4 * a + w] - d4[w]);
+                    ds[w] = pr[w] * da[4 * a + w];
                 }
                 pp[2 * a] = Elem<T>::pack(pr[0], pr[1]);
                 pp[2 * a + 1] = Elem<T>::pack(pr[2], pr[3]);
