@@ -527,7 +527,7 @@ def bench_bwd(args, name):
             "peak": PEAK_FP16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-            "traffic": counted_traffic(name, sources=BWD_SOURCES),
+            "traffic": counted_traffic(name, prefix="fa", sources=BWD_SOURCES),
         },
         "cpu_baseline": None,
     }

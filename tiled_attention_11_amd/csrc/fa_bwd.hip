@@ -23,16 +23,19 @@
 //    layout (one query per lane: its LSE and D_i are scalars), and
 //    dQ^T += K^T dS^T with K^T from transposing LDS reads
 //    (ds_read_b64_tr_b16) and dS^T straight from the accumulator.
-//  * fa_bwd_dkdv: the mirror image: a workgroup of 4 waves owns 128 keys (K^T, V^T
-//    fragments in registers, a key per lane) and streams the 64-query tiles
-//    of Q and dO that see them, with their LSE and D_i staged in LDS. Per
-//    32-query block: S = Q K^T and dP = dO V^T, then P and dS (a query per
-//    accumulator row), dV^T += dO^T P and dK^T += Q^T dS.
+//  * fa_bwd_dkdv: the mirror image: a workgroup of 8 waves owns 256 keys (32
+//    per wave, a key per lane; K^T fragments in registers, the workgroup's V
+//    rows in LDS) and streams the 32-query tiles of Q and dO that see them,
+//    with their LSE and -D_i staged in LDS. Per tile: S = Q K^T and
+//    dP = dO V^T, then P and dS (a query per accumulator row),
+//    dV^T += dO^T P and dK^T += Q^T dS.
 //  Each streamed tile is read both row-wise (MFMA A operand) and transposed
 //  (the A operand of the accumulating product), so it is stored twice, once
 //  per LDS swizzle, which keeps both read patterns free of bank conflicts.
-//  dQ and dK/dV each own their outputs, so there are no atomics and the
-//  results are deterministic.
+//  Hidden pairs get the exponent -inf by a select, never a branch. Both
+//  grids run their heaviest row tiles first across all heads. dQ and dK/dV
+//  each own their outputs, so there are no atomics and the results are
+//  deterministic.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
