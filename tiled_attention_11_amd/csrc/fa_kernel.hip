@@ -72,9 +72,11 @@ template <int D> struct Geom {
     static constexpr int CPR = RB / 16;                // 16-byte chunks per row
     static constexpr int TILE_BYTES = BN * RB;         // one K or V tile
     static constexpr int ROWS_PER_KB = 1024 / RB;      // rows per 1 KiB DMA block
-    static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / kWaves;
+    // A tile is 16 DMA blocks of 1 KiB; the four waves of one group issue them,
+    // four blocks each.
+    static constexpr int DMA_PER_WAVE = TILE_BYTES / 1024 / 4;
     static_assert(TILE_BYTES == 16384, "tile geometry");
-    static_assert(DMA_PER_WAVE * kWaves * 1024 == TILE_BYTES, "DMA split");
+    static_assert(DMA_PER_WAVE * 4 * 1024 == TILE_BYTES, "DMA split");
 
     static __device__ __forceinline__ int kchunk(int q, int r) { return dev::kchunk<D>(q, r); }
     static __device__ __forceinline__ int vchunk(int q, int r) { return dev::vchunk<D>(q, r); }
@@ -122,13 +124,13 @@ struct Kernel {
 
     static __device__ __forceinline__ void make_addr(Addr &ad, int wave, int lane, uint32_t rs) {
         const int l32 = lane & 31, g = lane >> 5;
-        // DMA block b = DMA_PER_WAVE * wave + i fills tile rows
+        // DMA block b = DMA_PER_WAVE * (wave % 4) + i fills tile rows
         // [b * ROWS_PER_KB, +ROWS_PER_KB); lane L lands in physical chunk
         // L % CPR of row L / CPR, so it fetches the logical chunk stored there.
         const int pc = lane % G::CPR;
 #pragma unroll
         for (int i = 0; i < G::DMA_PER_WAVE; ++i) {
-            const int row = (G::DMA_PER_WAVE * wave + i) * G::ROWS_PER_KB + lane / G::CPR;
+            const int row = (G::DMA_PER_WAVE * (wave & 3) + i) * G::ROWS_PER_KB + lane / G::CPR;
             ad.kdma[i] = row * rs + G::kchunk(pc, row) * 16;  // XOR swizzle is its own inverse
             ad.vdma[i] = row * rs + G::vchunk(pc, row) * 16;
         }
@@ -148,21 +150,33 @@ struct Kernel {
         }
     }
 
-    // Stream one K or V tile (rows k0 .. k0 + BN - 1 of the head whose row 0
-    // is at `h`, rows `rse` elements apart) into the LDS slot at byte address
-    // `slot`; `off` holds this lane's source offsets (which carry the matrix's
-    // swizzle). The buffer resource starts at row k0 and ends with row S - 1,
-    // so rows past the sequence read as zero.
-    static __device__ __forceinline__ void load_tile(const uint16_t *h, int k0, int S, int rse,
-                                                     uint32_t slot,
+    // The source of one K or V tile: rows k0 .. k0 + BN - 1 of the head whose
+    // row 0 is at `h`, rows `rse` elements apart, bound for the LDS slot at byte
+    // address `slot`. The buffer resource starts at row k0 and ends with row
+    // S - 1, so rows past the sequence read as zero (an empty resource, nrec 0,
+    // fills the slot with zeros and reads nothing).
+    struct TileSrc {
+        i32x4 rsrc;
+        uint32_t slot;
+    };
+    static __device__ __forceinline__ TileSrc tile_src(const uint16_t *h, int k0, int S, int rse,
+                                                       uint32_t slot, bool valid = true) {
+        const uint32_t nrec = !valid ? 0u
+                              : PACKED ? (uint32_t)(S - k0 - 1) * (uint32_t)rse * 2u + G::RB
+                                       : (uint32_t)(S - k0) * G::RB;
+        return TileSrc{buffer_rsrc(h + (int64_t)k0 * rse, nrec), slot};
+    }
+    // DMA block i (of DMA_PER_WAVE) of this wave's share of a tile; `off`
+    // holds the lane's source offset for it (which carries the matrix's swizzle).
+    static __device__ __forceinline__ void dma_block(const TileSrc &s, uint32_t off, int wave,
+                                                     int i) {
+        dma16(s.rsrc, s.slot + (uint32_t)(G::DMA_PER_WAVE * (wave & 3) + i) * 1024u, off);
+    }
+    static __device__ __forceinline__ void load_tile(const TileSrc &s,
                                                      const uint32_t (&off)[G::DMA_PER_WAVE],
                                                      int wave) {
-        const uint32_t nrec = PACKED ? (uint32_t)(S - k0 - 1) * (uint32_t)rse * 2u + G::RB
-                                     : (uint32_t)(S - k0) * G::RB;
-        const i32x4 rsrc = buffer_rsrc(h + (int64_t)k0 * rse, nrec);
 #pragma unroll
-        for (int i = 0; i < G::DMA_PER_WAVE; ++i)
-            dma16(rsrc, slot + (uint32_t)(G::DMA_PER_WAVE * wave + i) * 1024u, off[i]);
+        for (int i = 0; i < G::DMA_PER_WAVE; ++i) dma_block(s, off[i], wave, i);
     }
 
     // ---- work items -------------------------------------------------------------
@@ -352,18 +366,45 @@ struct Kernel {
                                                    uint32_t (&pk)[NKB][8], bool masked, int k0,
                                                    int qi, int S, int win_lo, int win_hi,
                                                    float c2, int g) {
-        // Accumulator element r of block kb holds key k0 + 32kb + 8(r/4) + 4g + r%4
-        // for query qi. A hidden score becomes -inf; with c2 > 0 its probability
-        // exp2(-inf) is exactly 0.
+        // Accumulator element r of block kb holds key k0 + 4g + off for query qi,
+        // off = 32kb + 8(r/4) + r%4 (a compile-time constant). The key is
+        // visible iff lo <= off <= hi, with lo = qi - win_lo - (k0 + 4g) and
+        // hi = min(qi + win_hi, S - 1) - (k0 + 4g); a hidden score becomes -inf
+        // (with c2 > 0 its probability exp2(-inf) is exactly 0). Per element
+        // that is a compare against a constant and a select, plus, when some
+        // lane's lower bound cuts into the tile (windows), a subtraction and an
+        // unsigned range compare. A tile that hides every key from the wave's
+        // rows leaves the softmax state as it is and gives P = 0.
         if (masked) {
+            const int base = k0 + 4 * g;
+            const int hi = min(qi + win_hi, S - 1) - base;
+            const int lo = qi - win_lo - base;
+            constexpr int kMaxOff = 32 * (NKB - 1) + 8 * 3 + 3;
+            if (!__builtin_amdgcn_ballot_w64(hi >= 0 && lo <= kMaxOff && hi >= lo)) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool ok = j < S && j <= qi + win_hi && j >= qi - win_lo;
-                    sacc[kb][r] = ok ? sacc[kb][r] : -INFINITY;
-                }
+                    for (int r = 0; r < 8; ++r) pk[kb][r] = 0u;
+                return;
+            }
+            if (!__builtin_amdgcn_ballot_w64(lo > 0)) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        sacc[kb][r] = off <= hi ? sacc[kb][r] : -INFINITY;
+                    }
+            } else {
+                const uint32_t w = (uint32_t)(hi - lo);  // > w unsigned: outside [lo, hi]
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+                        sacc[kb][r] = (uint32_t)(off - lo) <= w ? sacc[kb][r] : -INFINITY;
+                    }
+            }
         }
         // c2 > 0, so the maximum of the scaled scores is c2 times the maximum score.
         float smax = -INFINITY;
@@ -434,9 +475,9 @@ struct Kernel {
     }
 
     // The key loop of one wave. Global phases 0 .. 2T + 1 (T tiles) end at
-    // workgroup barriers. At phase 2i every wave issues its share of the DMA of
-    // K(i + 1) and V(i); at the end of phase 2i + 1 every wave waits for its own
-    // DMA, so after that barrier both tiles are in LDS. Group 0 runs M_i in
+    // workgroup barriers. In phase 2i the waves of group 0 issue the DMA of
+    // K(i + 1) and V(i) between their MFMAs; at the end of phase 2i + 1 every
+    // wave waits for its own DMA, so after that barrier both tiles are in LDS. Group 0 runs M_i in
     // phase 2i and V_i in phase 2i + 1; group 1 runs V_(i-1) in phase 2i and M_i
     // in phase 2i + 1. K(i) is read in phases 2i and 2i + 1, V(i) in phases
     // 2i + 2 and 2i + 3, so a slot is refilled only after both groups are done
@@ -458,20 +499,22 @@ struct Kernel {
             return (t >= t_in_lo && t < t_in_hi) ||
                    (k0 + BN - 1 <= S - 1 && k0 + BN - 1 <= r0 + win_hi && k0 >= rlast - win_lo);
         }
-        // Phase 2i: K(i + 1) (after the last tile, the next item's K(0), in the
-        // slot its parity continues into) and V(i); at phase 2 also the next
-        // item's Q (this item's Q has been read from the Q region by then).
-        __device__ __forceinline__ void dma(int i) const {
+        // The tiles streamed in phase 2i: K(i + 1) (after the last tile, the next
+        // item's K(0), in the slot its parity continues into; with no next item
+        // an empty source zero-fills the free slot) and V(i).
+        __device__ __forceinline__ TileSrc ksrc(int i) const {
             if (i + 1 < ntiles)
-                load_tile(kh, (t_first + i + 1) * BN, S, rse, smem_addr + kslot(kbase + i + 1),
-                          ad.kdma, wave);
-            else if (i + 1 == ntiles && nx.nt > 0)
-                load_tile(static_cast<const uint16_t *>(p.k) + head_base(S_all, nx),
-                          nx.t_first * BN, seq_len(S_all, nx), rse,
-                          smem_addr + kslot(kbase + ntiles), ad.kdma, wave);
-            if (i < ntiles)
-                load_tile(vh, (t_first + i) * BN, S, rse, smem_addr + vslot(kbase + i), ad.vdma,
-                          wave);
+                return tile_src(kh, (t_first + i + 1) * BN, S, rse, smem_addr + kslot(kbase + i + 1));
+            return tile_src(static_cast<const uint16_t *>(p.k) + head_base(S_all, nx),
+                            nx.t_first * BN, seq_len(S_all, nx), rse,
+                            smem_addr + kslot(kbase + i + 1), nx.nt > 0);
+        }
+        __device__ __forceinline__ TileSrc vsrc(int i) const {
+            return tile_src(vh, (t_first + i) * BN, S, rse, smem_addr + vslot(kbase + i));
+        }
+        // At phase 2 (called with i = 1 .. T): each wave's rows of the next
+        // item's Q (this item's Q has been read from the Q region by then).
+        __device__ __forceinline__ void dma_q_next(int i) const {
             if (i == 1 && nx.nt > 0)
                 dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, nx), nx.q0,
                       seq_len(S_all, nx), rse, smem_addr, wave, lane);
@@ -484,7 +527,11 @@ struct Kernel {
         // 16c + 8a + 4g + b for element 4a + b); its A operand comes from two
         // transposing reads, rows 16c + 4g + (0..3) and 16c + 8 + 4g + (0..3),
         // offsets that keep the V swizzle of the lane's base row.
-        template <bool QK, bool PV>
+        // With DMA (group 0, even phases 2i, i < T) the wave also issues its
+        // share of the tiles streamed in phase 2i, K(i + 1) then V(i), one 1 KiB
+        // block after every NS / 8 MFMAs: issued all at once by every wave, the
+        // 32 KiB queue up behind each other and stall the issuing waves.
+        template <bool QK, bool PV, bool DMA>
         __device__ __forceinline__ void mphase(State &st, f32x16 (&sacc)[NKB],
                                                const uint32_t (&pk)[NKB][8], int i) const {
             __builtin_amdgcn_s_setprio(1);
@@ -528,10 +575,23 @@ struct Kernel {
             };
 #pragma unroll
             for (int s = 0; s < kDist && s < NS; ++s) load(s);
+            constexpr int DPW = G::DMA_PER_WAVE;
+            constexpr int kPer = NS / (2 * DPW);  // MFMAs per DMA block
+            TileSrc kt{}, vt{};
+            if constexpr (DMA) {
+                kt = ksrc(i);
+                vt = vsrc(i);
+            }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s + kDist < NS) load(s + kDist);
                 mma(s);
+                if constexpr (DMA) {
+                    const int b = s / kPer;  // block b < DPW: K(i + 1), else V(i)
+                    if (s % kPer == kPer - 1)
+                        dma_block(b < DPW ? kt : vt, b < DPW ? ad.kdma[b % DPW] : ad.vdma[b % DPW],
+                                  wave, b % DPW);
+                }
             }
             // Issue order: the first kDist reads, then per slot its look-ahead
             // read(s) and its MFMA.
@@ -591,38 +651,36 @@ struct Kernel {
             uint32_t pk[NKB][8];
             const int nt = ntiles;  // >= 1
             if (GRP == 0) {
-                dma(0);
-                mphase<true, false>(st, sacc, pk, 0);
+                mphase<true, false, true>(st, sacc, pk, 0);
                 end_phase(false);
                 vphase(st, sacc, pk, 0);
                 end_phase(true);
                 for (int i = 1; i < nt; ++i) {
-                    dma(i);
-                    mphase<true, true>(st, sacc, pk, i);
+                    dma_q_next(i);
+                    mphase<true, true, true>(st, sacc, pk, i);
                     end_phase(false);
                     vphase(st, sacc, pk, i);
                     end_phase(true);
                 }
-                dma(nt);
-                mphase<false, true>(st, sacc, pk, nt);
+                dma_q_next(nt);
+                mphase<false, true, false>(st, sacc, pk, nt);
                 end_phase(false);
                 end_phase(true);
             } else {
-                dma(0);
                 end_phase(false);
-                mphase<true, false>(st, sacc, pk, 0);
+                mphase<true, false, false>(st, sacc, pk, 0);
                 end_phase(true);
                 for (int i = 1; i < nt; ++i) {
-                    dma(i);
+                    dma_q_next(i);
                     vphase(st, sacc, pk, i - 1);
                     end_phase(false);
-                    mphase<true, true>(st, sacc, pk, i);
+                    mphase<true, true, false>(st, sacc, pk, i);
                     end_phase(true);
                 }
-                dma(nt);
+                dma_q_next(nt);
                 vphase(st, sacc, pk, nt - 1);
                 end_phase(false);
-                mphase<false, true>(st, sacc, pk, nt);
+                mphase<false, true, false>(st, sacc, pk, nt);
                 end_phase(true);
             }
         }
@@ -666,8 +724,10 @@ struct Kernel {
         Item it = next_item(p, tab, wk, r);
         if (PACKED && it.nt == 0) return;  // every sequence is shorter than the workgroup's share
         {
-            load_tile(static_cast<const uint16_t *>(p.k) + head_base(S_all, it), it.t_first * BN,
-                      seq_len(S_all, it), rse, smem_addr + kslot(0), ad.kdma, wave);
+            if (grp == 0)
+                load_tile(tile_src(static_cast<const uint16_t *>(p.k) + head_base(S_all, it),
+                                   it.t_first * BN, seq_len(S_all, it), rse, smem_addr + kslot(0)),
+                          ad.kdma, wave);
             dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, it), it.q0,
                   seq_len(S_all, it), rse, smem_addr, wave, lane);
             __builtin_amdgcn_s_waitcnt(0);
