@@ -781,21 +781,37 @@ struct Kernel {
 
             // ---- epilogue: O = O_acc / l, LSE = ln 2 * (m + log2 l) ----
             const float l_tot = sum_with_partner(st.l_run);
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            // Elements 4a .. 4a + 3 of block db hold dims 32db + 8a + 4g + 0..3 of
+            // the row, which lanes l and l ^ 32 share. For each pair of 8-dim
+            // chunks (2c, 2c + 1) the two lanes trade halves (v_permlane32_swap
+            // trades lanes 32-63 of its first operand with lanes 0-31 of its
+            // second), so that lane half g holds chunk 2c + g whole and stores it
+            // with one 16-byte write: 32 contiguous bytes of a row per pair of
+            // lanes instead of 16 (the O stores otherwise stall the epilogue).
+            u32x4 ow[NDB][2];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const f32x16 &a = st.oacc[db];
+                    const int e0 = 8 * c, e1 = 8 * c + 4;  // chunks 2c and 2c + 1
+                    const uint32_t x00 = Elem<T>::pack(a[e0 + 0] * inv, a[e0 + 1] * inv);
+                    const uint32_t x01 = Elem<T>::pack(a[e0 + 2] * inv, a[e0 + 3] * inv);
+                    const uint32_t x10 = Elem<T>::pack(a[e1 + 0] * inv, a[e1 + 1] * inv);
+                    const uint32_t x11 = Elem<T>::pack(a[e1 + 2] * inv, a[e1 + 3] * inv);
+                    const auto r0 = __builtin_amdgcn_permlane32_swap(x00, x10, false, false);
+                    const auto r1 = __builtin_amdgcn_permlane32_swap(x01, x11, false, false);
+                    ow[db][c] = u32x4{(uint32_t)r0[0], (uint32_t)r1[0], (uint32_t)r0[1],
+                                      (uint32_t)r1[1]};
+                }
             if (qi < S) {
-                const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
                 uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * rse;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        // elements 4a .. 4a+3 hold dims 32db + 8a + 4g + 0..3
-                        u32x2 w;
-                        w[0] = Elem<T>::pack(st.oacc[db][4 * a + 0] * inv,
-                                             st.oacc[db][4 * a + 1] * inv);
-                        w[1] = Elem<T>::pack(st.oacc[db][4 * a + 2] * inv,
-                                             st.oacc[db][4 * a + 3] * inv);
-                        *reinterpret_cast<u32x2 *>(orow + 32 * db + 8 * a + 4 * g) = w;
-                    }
+                    for (int c = 0; c < 2; ++c)
+                        *reinterpret_cast<u32x4 *>(orow + 32 * db + 16 * c + 8 * g) = ow[db][c];
                 if (p.lse && g == 0) {
                     const float lse = l_tot > 0.0f
                                           ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
