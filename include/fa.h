@@ -100,8 +100,7 @@ typedef enum {
  * overlap q, k, v or each other (checked on the host).
  * Arithmetic: QK^T and PV run on fp16/bf16 matrix cores with fp32 accumulation;
  * softmax state is fp32; probabilities are rounded once to `dtype` for PV. The
- * row sum (and so the LSE) adds, in fp32, the fp16-rounded probabilities for
- * fp16 (an LSE change below 2.5e-4) and the unrounded ones for bf16. Results
+ * row sum (and so the LSE) adds the unrounded fp32 probabilities. Results
  * are bitwise deterministic for a given input, device and library build.
  * Returns FA_OK or a negative fa_status.
  */

@@ -430,12 +430,10 @@ struct Kernel {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -mu));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, -mu));
                 pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
-                if (!Elem<T>::kSumRounded) {
-                    psum0 += p0;
-                    psum1 += p1;
-                }
+                psum0 += p0;
+                psum1 += p1;
             }
-        if (!Elem<T>::kSumRounded) st.l_run += psum0 + psum1;
+        st.l_run += psum0 + psum1;
     }
 
     // LDS: two K slots then two V slots; relative tile i uses slot i & 1.
@@ -607,20 +605,6 @@ struct Kernel {
                     else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
                 __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
-            }
-            // The row sum of tile i - 1 from its rounded probabilities (fp16): VALU
-            // work that issues between this wave's MFMAs.
-            if (PV && Elem<T>::kSumRounded) {
-                float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 8; r += 2) {
-                        s0 = Elem<T>::sum2(pk[kb][r], s0);
-                        s1 = Elem<T>::sum2(pk[kb][r + 1], s1);
-                    }
-                st.l_run += s0 + s1;
-                pin(st.l_run);
             }
             if (QK) pin(sacc);
             if (PV) pin(st.oacc);
