@@ -101,7 +101,6 @@ struct Kernel {
         f32x16 oacc[NDB];   // O^T accumulator: lane holds query l32, dims of its C layout
         float m_run;        // reference maximum of the base-2 scaled scores
         float l_run;        // this lane's share of the row sum, relative to m_run
-        float alpha;        // pending rescale of oacc to the reference m_run
     };
 
     // Per-lane byte offsets, fixed for the whole key loop.
@@ -414,12 +413,17 @@ struct Kernel {
             for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sacc[kb][r]);
         smax = max_with_partner(smax);
         const float m_tile = (smax == -INFINITY) ? -INFINITY : smax * c2;
-        // O is rescaled by the next MFMA phase (st.alpha), before its P V.
+        // O (which holds the tiles before this one) and l move to the new
+        // reference here, in the softmax phase, so the MFMA phase carries no
+        // rescale check.
         if (__builtin_amdgcn_ballot_w64(m_tile > st.m_run + kRescaleSlack)) {
             const float m_new = fmaxf(st.m_run, m_tile);
-            st.alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+            const float alpha =
+                (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
             st.m_run = m_new;
-            st.l_run *= st.alpha;
+            st.l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) st.oacc[db] *= alpha;
         }
         const float mu = (st.m_run == -INFINITY) ? 0.0f : st.m_run;
         float psum0 = 0.0f, psum1 = 0.0f;
@@ -517,9 +521,7 @@ struct Kernel {
                 dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, nx), nx.q0,
                       seq_len(S_all, nx), rse, smem_addr, wave, lane);
         }
-        // M_i: O takes the rescale the softmax of tile i - 1 asked for (a wave-
-        // uniform branch, rarely taken once the row maxima settle), then
-        // O^T += V^T P^T of tile i - 1 and S^T = K Q^T of tile i, as one stream
+        // M_i: O^T += V^T P^T of tile i - 1 and S^T = K Q^T of tile i, as one stream
         // of MFMAs whose LDS operands are read kDist MFMAs ahead. P V chunk c's
         // B operand is P^T elements 8(c%2) .. +7 of score block c/2 (keys
         // 16c + 8a + 4g + b for element 4a + b); its A operand comes from two
@@ -533,11 +535,6 @@ struct Kernel {
         __device__ __forceinline__ void mphase(State &st, f32x16 (&sacc)[NKB],
                                                const uint32_t (&pk)[NKB][8], int i) const {
             __builtin_amdgcn_s_setprio(1);
-            if (PV && __builtin_amdgcn_ballot_w64(st.alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) st.oacc[db] *= st.alpha;
-                st.alpha = 1.0f;
-            }
             const LDS char *vs = smem + vslot(kbase + i - 1);
             const LDS char *ks = smem + kslot(kbase + i);
             constexpr int NPV = PV ? NPC * NDB : 0;  // MFMA slot s < NPV: P V chunk s / NDB, block s % NDB
@@ -617,7 +614,6 @@ struct Kernel {
             pin(pk);
             pin(st.l_run);
             pin(st.m_run);
-            pin(st.alpha);
         }
         // A bare barrier: the kernel orders its own LDS traffic. Every LDS read
         // of a phase has returned before the phase ends (the pinned MFMA
@@ -753,7 +749,6 @@ struct Kernel {
             for (int db = 0; db < NDB; ++db) st.oacc[db] = f32x16{};
             st.m_run = -INFINITY;
             st.l_run = 0.0f;
-            st.alpha = 1.0f;
 
             Loop loop{p,     smem,   smem_addr, kh, vh,   S,  S_all,  rse, it.t_first, it.nt,
                       it.t_in_lo, it.t_in_hi, r0, rlast, qi, win_lo, win_hi, c2,  g, wave,
