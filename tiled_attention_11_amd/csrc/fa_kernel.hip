@@ -361,10 +361,13 @@ struct Kernel {
     // and l when some row's maximum outgrows the slack (always on the first
     // visible tile, where m_run is -inf), and the probabilities: rounded once
     // to the MFMA operand type into pk, summed unrounded into l.
+    // dma(b), b = 0 .. 3, issues one DMA block of the caller's; the four calls
+    // are spread over the exponentials (all of them, in order, on every path).
+    template <typename Dma>
     static __device__ __forceinline__ void softmax(State &st, f32x16 (&sacc)[NKB],
                                                    uint32_t (&pk)[NKB][8], bool masked, int k0,
                                                    int qi, int S, int win_lo, int win_hi,
-                                                   float c2, int g) {
+                                                   float c2, int g, const Dma &dma) {
         // Accumulator element r of block kb holds key k0 + 4g + off for query qi,
         // off = 32kb + 8(r/4) + r%4 (a compile-time constant). The key is
         // visible iff lo <= off <= hi, with lo = qi - win_lo - (k0 + 4g) and
@@ -384,6 +387,8 @@ struct Kernel {
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 8; ++r) pk[kb][r] = 0u;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) dma(b);
                 return;
             }
             if (!__builtin_amdgcn_ballot_w64(lo > 0)) {
@@ -436,6 +441,9 @@ struct Kernel {
                 pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
                 psum0 += p0;
                 psum1 += p1;
+                constexpr int kIters = NKB * 8;  // exponential pairs per lane
+                const int it = kb * 8 + (r >> 1);
+                if (it % (kIters / 4) == kIters / 4 - 1) dma(it / (kIters / 4));
             }
         st.l_run += psum0 + psum1;
     }
@@ -478,8 +486,9 @@ struct Kernel {
 
     // The key loop of one wave. Global phases 0 .. 2T + 1 (T tiles) end at
     // workgroup barriers. In phase 2i the waves of group 0 issue the DMA of
-    // K(i + 1) and V(i) between their MFMAs; at the end of phase 2i + 1 every
-    // wave waits for its own DMA, so after that barrier both tiles are in LDS. Group 0 runs M_i in
+    // K(i + 1) between their MFMAs and those of group 1 the DMA of V(i) between
+    // their exponentials; at the end of phase 2i + 1 every wave waits for its
+    // own DMA, so after that barrier both tiles are in LDS. Group 0 runs M_i in
     // phase 2i and V_i in phase 2i + 1; group 1 runs V_(i-1) in phase 2i and M_i
     // in phase 2i + 1. K(i) is read in phases 2i and 2i + 1, V(i) in phases
     // 2i + 2 and 2i + 3, so a slot is refilled only after both groups are done
@@ -528,9 +537,10 @@ struct Kernel {
         // transposing reads, rows 16c + 4g + (0..3) and 16c + 8 + 4g + (0..3),
         // offsets that keep the V swizzle of the lane's base row.
         // With DMA (group 0, even phases 2i, i < T) the wave also issues its
-        // share of the tiles streamed in phase 2i, K(i + 1) then V(i), one 1 KiB
-        // block after every NS / 8 MFMAs: issued all at once by every wave, the
-        // 32 KiB queue up behind each other and stall the issuing waves.
+        // share of K(i + 1), one 1 KiB block after every NS / 4 MFMAs (group 1
+        // streams V(i) from its softmax phase): issued all at once by every
+        // wave, the 32 KiB of a phase queue up behind each other and stall the
+        // issuing waves.
         template <bool QK, bool PV, bool DMA>
         __device__ __forceinline__ void mphase(State &st, f32x16 (&sacc)[NKB],
                                                const uint32_t (&pk)[NKB][8], int i) const {
@@ -571,22 +581,15 @@ struct Kernel {
 #pragma unroll
             for (int s = 0; s < kDist && s < NS; ++s) load(s);
             constexpr int DPW = G::DMA_PER_WAVE;
-            constexpr int kPer = NS / (2 * DPW);  // MFMAs per DMA block
-            TileSrc kt{}, vt{};
-            if constexpr (DMA) {
-                kt = ksrc(i);
-                vt = vsrc(i);
-            }
+            constexpr int kPer = NS / DPW;  // MFMAs per DMA block
+            TileSrc kt{};
+            if constexpr (DMA) kt = ksrc(i);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s + kDist < NS) load(s + kDist);
                 mma(s);
-                if constexpr (DMA) {
-                    const int b = s / kPer;  // block b < DPW: K(i + 1), else V(i)
-                    if (s % kPer == kPer - 1)
-                        dma_block(b < DPW ? kt : vt, b < DPW ? ad.kdma[b % DPW] : ad.vdma[b % DPW],
-                                  wave, b % DPW);
-                }
+                if constexpr (DMA)
+                    if (s % kPer == kPer - 1) dma_block(kt, ad.kdma[s / kPer], wave, s / kPer);
             }
             // Issue order: the first kDist reads, then per slot its look-ahead
             // read(s) and its MFMA.
@@ -607,10 +610,18 @@ struct Kernel {
             if (PV) pin(st.oacc);
             __builtin_amdgcn_s_setprio(0);
         }
+        // With DMA (group 1 in even phases 2i + 2, i + 1 < T) the wave issues its
+        // share of V(i + 1), one block after each quarter of the exponentials.
+        template <bool DMA>
         __device__ __forceinline__ void vphase(State &st, f32x16 (&sacc)[NKB],
                                                uint32_t (&pk)[NKB][8], int i) const {
             const int t = t_first + i;
-            softmax(st, sacc, pk, !tile_full(t), t * BN, qi, S, win_lo, win_hi, c2, g);
+            TileSrc vt{};
+            if constexpr (DMA) vt = vsrc(i + 1);
+            const auto dma = [&](int b) {
+                if constexpr (DMA) dma_block(vt, ad.vdma[b], wave, b);
+            };
+            softmax(st, sacc, pk, !tile_full(t), t * BN, qi, S, win_lo, win_hi, c2, g, dma);
             pin(pk);
             pin(st.l_run);
             pin(st.m_run);
@@ -633,13 +644,13 @@ struct Kernel {
             if (GRP == 0) {
                 mphase<true, false, true>(st, sacc, pk, 0);
                 end_phase(false);
-                vphase(st, sacc, pk, 0);
+                vphase<false>(st, sacc, pk, 0);
                 end_phase(true);
                 for (int i = 1; i < nt; ++i) {
                     dma_q_next(i);
                     mphase<true, true, true>(st, sacc, pk, i);
                     end_phase(false);
-                    vphase(st, sacc, pk, i);
+                    vphase<false>(st, sacc, pk, i);
                     end_phase(true);
                 }
                 dma_q_next(nt);
@@ -647,18 +658,19 @@ struct Kernel {
                 end_phase(false);
                 end_phase(true);
             } else {
+                load_tile(vsrc(0), ad.vdma, wave);
                 end_phase(false);
                 mphase<true, false, false>(st, sacc, pk, 0);
                 end_phase(true);
                 for (int i = 1; i < nt; ++i) {
                     dma_q_next(i);
-                    vphase(st, sacc, pk, i - 1);
+                    vphase<true>(st, sacc, pk, i - 1);
                     end_phase(false);
                     mphase<true, true, false>(st, sacc, pk, i);
                     end_phase(true);
                 }
                 dma_q_next(nt);
-                vphase(st, sacc, pk, nt - 1);
+                vphase<false>(st, sacc, pk, nt - 1);
                 end_phase(false);
                 mphase<false, true, false>(st, sacc, pk, nt);
                 end_phase(true);
