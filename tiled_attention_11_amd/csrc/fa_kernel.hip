@@ -462,8 +462,10 @@ struct Kernel {
     // its part of the Q region. Lane L of 1 KiB block b lands in physical
     // chunk L % CPR of region row b * ROWS_PER_KB + L / CPR, so it fetches the
     // logical chunk that the K swizzle stores there.
+    // Blocks [b0, b1) of the wave's kQBlocks.
     static __device__ __forceinline__ void dma_q(const uint16_t *qh, int q0, int S, int rse,
-                                                 uint32_t smem_addr, int wave, int lane) {
+                                                 uint32_t smem_addr, int wave, int lane,
+                                                 int b0 = 0, int b1 = kQBlocks) {
         const int r0 = q0 + wave * kWaveRows;
         // A wave whose rows all lie past S gets an empty resource: every read
         // returns zero and nothing past the tensor is touched.
@@ -476,8 +478,9 @@ struct Kernel {
 #pragma unroll
         for (int b = 0; b < kQBlocks; ++b) {
             const int row = b * G::ROWS_PER_KB + lane / G::CPR;
-            dma16(rsrc, base + (uint32_t)b * 1024u,
-                  (uint32_t)row * (uint32_t)rse * 2u + (uint32_t)(G::kchunk(pc, row) * 16));
+            if (b >= b0 && b < b1)
+                dma16(rsrc, base + (uint32_t)b * 1024u,
+                      (uint32_t)row * (uint32_t)rse * 2u + (uint32_t)(G::kchunk(pc, row) * 16));
         }
     }
     static __device__ __forceinline__ uint32_t vslot(int i) {
@@ -523,12 +526,17 @@ struct Kernel {
         __device__ __forceinline__ TileSrc vsrc(int i) const {
             return tile_src(vh, (t_first + i) * BN, S, rse, smem_addr + vslot(kbase + i));
         }
-        // At phase 2 (called with i = 1 .. T): each wave's rows of the next
-        // item's Q (this item's Q has been read from the Q region by then).
+        // At phases 2i, i = 1 .. T: each wave's rows of the next item's Q, two
+        // 1 KiB blocks per phase (the rest at phase 2T), so that no phase
+        // stalls on a burst of DMA. This item's Q has left the Q region (for
+        // registers) before phase 0 ends.
         __device__ __forceinline__ void dma_q_next(int i) const {
-            if (i == 1 && nx.nt > 0)
+            constexpr int kPerPhase = 2;
+            const int b0 = kPerPhase * (i - 1);
+            const int b1 = i == ntiles ? kQBlocks : kPerPhase * i;
+            if (nx.nt > 0 && b0 < kQBlocks)
                 dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, nx), nx.q0,
-                      seq_len(S_all, nx), rse, smem_addr, wave, lane);
+                      seq_len(S_all, nx), rse, smem_addr, wave, lane, b0, b1);
         }
         // M_i: O^T += V^T P^T of tile i - 1 and S^T = K Q^T of tile i, as one stream
         // of MFMAs whose LDS operands are read kDist MFMAs ahead. P V chunk c's
