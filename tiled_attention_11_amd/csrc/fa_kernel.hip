@@ -15,12 +15,13 @@
 // gfx950 design (not the pages' Ascend design):
 //  * One workgroup = 8 waves of 64 lanes = 256 query rows of one (b, h);
 //    each wave owns 32 query rows for the whole key loop. The waves form two
-//    groups (0-3 and 4-7, one wave of each per SIMD) that alternate, at
-//    workgroup barriers, between an MFMA phase (P V of the previous key tile,
-//    then the scores of the next) and a VALU phase (mask and online softmax),
-//    so that on every SIMD one wave keeps the matrix core busy while the other
-//    computes exponentials: a single wave cannot issue VALU work fast enough
-//    to hide it under its own MFMAs, but two waves of a SIMD co-issue.
+//    groups (0-3 and 4-7, one wave of each per SIMD) that alternate between
+//    an MFMA phase (P V of the previous key tile, then the scores of the next)
+//    and a VALU phase (mask and online softmax), in opposite order within
+//    each step of the key loop (one workgroup barrier per step), so that on
+//    every SIMD one wave keeps the matrix core busy while the other computes
+//    exponentials: a single wave cannot issue VALU work fast enough to hide
+//    it under its own MFMAs, but two waves of a SIMD co-issue.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16
 //    (A = 32 keys x 16 dims, B = 16 dims x 32 queries). In the accumulator
 //    layout lane l holds query l % 32 and 16 keys, so the row max and row sum
@@ -348,14 +349,15 @@ struct Kernel {
 
     // ---- phases -----------------------------------------------------------------
     // The workgroup's eight waves form two groups (waves 0-3 and 4-7; one wave
-    // of each group per SIMD) that alternate between two kinds of work at
-    // workgroup barriers, so that on every SIMD one wave keeps the matrix core
-    // busy while the other runs the softmax on the VALU:
+    // of each group per SIMD) that alternate between two kinds of work, so
+    // that on every SIMD one wave keeps the matrix core busy while the other
+    // runs the softmax on the VALU:
     //   M_m: O^T += V^T P^T of tile m - 1, then S^T = K Q^T of tile m (MFMA);
     //   V_m: mask, online softmax and P of tile m (VALU).
-    // A group runs M_0, V_0, M_1, V_1, ..., M_T; group 1 starts one phase after
-    // group 0. K(t) is read in phases 2t and 2t + 1, V(t) in 2t + 2 and 2t + 3;
-    // both stream in (DMA) two phases ahead and are double-buffered.
+    // A group runs M_0, V_0, M_1, V_1, ..., M_T; group 1 runs each one phase
+    // after group 0. Step i (one workgroup barrier at its end) holds M_i, V_i
+    // of group 0 and V_(i-1), M_i of group 1. K(t) and V(t - 1) are read in
+    // step t; both stream in (DMA) a step ahead and are double-buffered.
 
     // Softmax of one tile: mask (boundary tiles), tile maximum, rescale of O
     // and l when some row's maximum outgrows the slack (always on the first
@@ -487,15 +489,16 @@ struct Kernel {
         return (2 + (i & 1)) * G::TILE_BYTES;
     }
 
-    // The key loop of one wave. Global phases 0 .. 2T + 1 (T tiles) end at
-    // workgroup barriers. In phase 2i the waves of group 0 issue the DMA of
-    // K(i + 1) between their MFMAs and those of group 1 the DMA of V(i) between
-    // their exponentials; at the end of phase 2i + 1 every wave waits for its
-    // own DMA, so after that barrier both tiles are in LDS. Group 0 runs M_i in
-    // phase 2i and V_i in phase 2i + 1; group 1 runs V_(i-1) in phase 2i and M_i
-    // in phase 2i + 1. K(i) is read in phases 2i and 2i + 1, V(i) in phases
-    // 2i + 2 and 2i + 3, so a slot is refilled only after both groups are done
-    // with its previous tile.
+    // The key loop of one wave: steps 0 .. T (T tiles), each ended by a
+    // workgroup barrier. In step i group 0 runs M_i then V_i, group 1 runs
+    // V_(i-1) then M_i, so on each SIMD the two waves' MFMA and softmax phases
+    // interleave with no barrier between them. In step i the waves of group 0
+    // issue the DMA of K(i + 1) between their MFMAs and those of group 1 the
+    // DMA of V(i) between their exponentials; at the end of the step every wave
+    // waits for its own DMA, so after that barrier both tiles are in LDS.
+    // Step i reads K(i) and V(i - 1) and writes K(i + 1) and V(i) into the
+    // slots of K(i - 1) and V(i - 2), which step i - 1 read: the barrier
+    // between the steps orders every refill after the reads it replaces.
     struct Loop {
         const FwdParams &p;
         const LDS char *smem;
@@ -513,7 +516,7 @@ struct Kernel {
             return (t >= t_in_lo && t < t_in_hi) ||
                    (k0 + BN - 1 <= S - 1 && k0 + BN - 1 <= r0 + win_hi && k0 >= rlast - win_lo);
         }
-        // The tiles streamed in phase 2i: K(i + 1) (after the last tile, the next
+        // The tiles streamed in step i: K(i + 1) (after the last tile, the next
         // item's K(0), in the slot its parity continues into; with no next item
         // an empty source zero-fills the free slot) and V(i).
         __device__ __forceinline__ TileSrc ksrc(int i) const {
@@ -526,10 +529,10 @@ struct Kernel {
         __device__ __forceinline__ TileSrc vsrc(int i) const {
             return tile_src(vh, (t_first + i) * BN, S, rse, smem_addr + vslot(kbase + i));
         }
-        // At phases 2i, i = 1 .. T: each wave's rows of the next item's Q, two
-        // 1 KiB blocks per phase (the rest at phase 2T), so that no phase
-        // stalls on a burst of DMA. This item's Q has left the Q region (for
-        // registers) before phase 0 ends.
+        // At steps i = 1 .. T: each wave's rows of the next item's Q, two 1 KiB
+        // blocks per step (the rest at step T), so that no step stalls on a
+        // burst of DMA. This item's Q has left the Q region (for registers)
+        // before step 0 ends.
         __device__ __forceinline__ void dma_q_next(int i) const {
             constexpr int kPerPhase = 2;
             const int b0 = kPerPhase * (i - 1);
@@ -544,7 +547,7 @@ struct Kernel {
         // 16c + 8a + 4g + b for element 4a + b); its A operand comes from two
         // transposing reads, rows 16c + 4g + (0..3) and 16c + 8 + 4g + (0..3),
         // offsets that keep the V swizzle of the lane's base row.
-        // With DMA (group 0, even phases 2i, i < T) the wave also issues its
+        // With DMA (group 0, step i < T) the wave also issues its
         // share of K(i + 1), one 1 KiB block after every NS / 4 MFMAs (group 1
         // streams V(i) from its softmax phase): issued all at once by every
         // wave, the 32 KiB of a phase queue up behind each other and stall the
@@ -618,7 +621,7 @@ struct Kernel {
             if (PV) pin(st.oacc);
             __builtin_amdgcn_s_setprio(0);
         }
-        // With DMA (group 1 in even phases 2i + 2, i + 1 < T) the wave issues its
+        // With DMA (group 1 in step i + 1, i + 1 < T) the wave issues its
         // share of V(i + 1), one block after each quarter of the exponentials.
         template <bool DMA>
         __device__ __forceinline__ void vphase(State &st, f32x16 (&sacc)[NKB],
@@ -634,13 +637,12 @@ struct Kernel {
             pin(st.l_run);
             pin(st.m_run);
         }
-        // A bare barrier: the kernel orders its own LDS traffic. Every LDS read
-        // of a phase has returned before the phase ends (the pinned MFMA
-        // results consumed them), so a slot may be refilled after the barrier;
-        // DMA'd tiles are waited for (vmcnt) only at the end of odd phases,
-        // which leaves each DMA two phases to land.
-        static __device__ __forceinline__ void end_phase(bool wait) {
-            if (wait) __builtin_amdgcn_s_waitcnt(0);
+        // The end of a step: this wave's DMA has landed, then a bare barrier
+        // (the kernel orders its own LDS traffic: every LDS read of a step has
+        // returned before the step ends, the pinned MFMA results consumed
+        // them, so a slot may be refilled after the barrier).
+        static __device__ __forceinline__ void end_step() {
+            __builtin_amdgcn_s_waitcnt(0);
             __builtin_amdgcn_s_barrier();
         }
 
@@ -651,37 +653,31 @@ struct Kernel {
             const int nt = ntiles;  // >= 1
             if (GRP == 0) {
                 mphase<true, false, true>(st, sacc, pk, 0);
-                end_phase(false);
                 vphase<false>(st, sacc, pk, 0);
-                end_phase(true);
+                end_step();
                 for (int i = 1; i < nt; ++i) {
                     dma_q_next(i);
                     mphase<true, true, true>(st, sacc, pk, i);
-                    end_phase(false);
                     vphase<false>(st, sacc, pk, i);
-                    end_phase(true);
+                    end_step();
                 }
                 dma_q_next(nt);
                 mphase<false, true, false>(st, sacc, pk, nt);
-                end_phase(false);
-                end_phase(true);
+                end_step();
             } else {
                 load_tile(vsrc(0), ad.vdma, wave);
-                end_phase(false);
                 mphase<true, false, false>(st, sacc, pk, 0);
-                end_phase(true);
+                end_step();
                 for (int i = 1; i < nt; ++i) {
                     dma_q_next(i);
                     vphase<true>(st, sacc, pk, i - 1);
-                    end_phase(false);
                     mphase<true, true, false>(st, sacc, pk, i);
-                    end_phase(true);
+                    end_step();
                 }
                 dma_q_next(nt);
                 vphase<false>(st, sacc, pk, nt - 1);
-                end_phase(false);
                 mphase<false, true, false>(st, sacc, pk, nt);
-                end_phase(true);
+                end_step();
             }
         }
     };
