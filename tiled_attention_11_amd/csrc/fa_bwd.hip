@@ -218,6 +218,18 @@ struct Bwd {
             load_tile<kTrSwz, kDqWaves, BN>(kh, t * BN, S, st + G::TILE_BYTES, wave, lane);
             load_tile<kRowSwz, kDqWaves, BN>(vh, t * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
         };
+        // Within a step the next tile's DMA goes in two parts, K and V rows
+        // after the barrier and K transposed half-way through the key blocks,
+        // so that no wave stalls behind a 48 KiB burst.
+        auto issue_k = [&](int t, int s) {
+            const uint32_t st = sbase + s * kDqStage;
+            load_tile<kRowSwz, kDqWaves, BN>(kh, t * BN, S, st, wave, lane);
+            load_tile<kRowSwz, kDqWaves, BN>(vh, t * BN, S, st + 2 * G::TILE_BYTES, wave, lane);
+        };
+        auto issue_kt = [&](int t, int s) {
+            const uint32_t st = sbase + s * kDqStage;
+            load_tile<kTrSwz, kDqWaves, BN>(kh, t * BN, S, st + G::TILE_BYTES, wave, lane);
+        };
 
         f32x16 acc[NDB];
 #pragma unroll
@@ -227,12 +239,13 @@ struct Bwd {
             const int s = (t - t_first) & 1;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // tile t is in LDS; every wave is done with stage s ^ 1
-            if (t < t_last) issue(t + 1, s ^ 1);
+            if (t < t_last) issue_k(t + 1, s ^ 1);
             const LDS char *kr = smem + s * kDqStage;
             const LDS char *kt = kr + G::TILE_BYTES;
             const LDS char *vr = kr + 2 * G::TILE_BYTES;
 #pragma unroll
             for (int sb = 0; sb < NSB; ++sb) {
+                if (sb == NSB / 2 && t < t_last) issue_kt(t + 1, s ^ 1);
                 // Per wave (uniform): a key block that none of the wave's rows
                 // sees is skipped; one that all of them see in full is not masked.
                 const int kb0 = t * BN + 32 * sb, kb1 = min(kb0 + 31, S - 1);
@@ -333,6 +346,19 @@ struct Bwd {
             load_tile<kRowSwz, kKvWaves, QB>(doh, u * QB, S, st + 2 * GQ::TILE_BYTES, wave, lane);
             load_tile<kTrSwz, kKvWaves, QB>(doh, u * QB, S, st + 3 * GQ::TILE_BYTES, wave, lane);
         };
+        // Within a step the next tile's DMA goes in two halves, Q after the
+        // barrier and dO after the S and dP products: issued at once by every
+        // wave, the 32 KiB queue up and stall the issuing waves.
+        auto issue_q = [&](int u, int s) {
+            const uint32_t st = sbase + kKvV + s * kKvStage;
+            load_tile<kRowSwz, kKvWaves, QB>(qh, u * QB, S, st, wave, lane);
+            load_tile<kTrSwz, kKvWaves, QB>(qh, u * QB, S, st + GQ::TILE_BYTES, wave, lane);
+        };
+        auto issue_do = [&](int u, int s) {
+            const uint32_t st = sbase + kKvV + s * kKvStage;
+            load_tile<kRowSwz, kKvWaves, QB>(doh, u * QB, S, st + 2 * GQ::TILE_BYTES, wave, lane);
+            load_tile<kTrSwz, kKvWaves, QB>(doh, u * QB, S, st + 3 * GQ::TILE_BYTES, wave, lane);
+        };
         // the tile's LSE (base 2) and D_i: fetched by the first QB threads,
         // stored into the stage's arrays once they arrive
         auto fetch_vec = [&](int u, float &l2, float &dr) {
@@ -364,7 +390,7 @@ struct Bwd {
             float nl2 = 0.0f, ndr = 0.0f;
             const bool more = u < u_last;
             if (more) {
-                issue(u + 1, s ^ 1);
+                issue_q(u + 1, s ^ 1);
                 if (threadIdx.x < QB) fetch_vec(u + 1, nl2, ndr);
             }
             const LDS char *qr = smem + kKvV + s * kKvStage;
@@ -385,6 +411,7 @@ struct Bwd {
                 sa = Elem<T>::mma(read_rows(qr, o, 0, c), kf[c], sa);
                 da = Elem<T>::mma(read_rows(dor, o, 0, c), read_rows(vw, o, 0, c), da);
             }
+            if (more) issue_do(u + 1, s ^ 1);
             // element e: query u*QB + 8(e/4) + 4g + e%4, key kj. Hidden pairs:
             // exponent -inf by selects under one uniform branch, as in dq.
             float x[16];
