@@ -77,6 +77,31 @@ struct Bwd {
     static constexpr int NDB = D / 32;   // 32-dim output blocks
     static constexpr int NSB = BN / 32;  // 32-row blocks of a streamed tile
 
+    // Element e of a lane's 32 x 32 accumulator block sits at index
+    // base + 8(e/4) + e%4 along the streamed dimension; the pair is visible iff
+    // that index lies in [first, last]. The offsets are compile-time constants,
+    // so a hidden exponent becomes -inf by one compare and select per element
+    // (plus a subtraction and an unsigned range compare when some lane's lower
+    // bound cuts into the block).
+    static __device__ __forceinline__ void mask_block(float (&x)[16], int base, int first,
+                                                      int last) {
+        const int lo = first - base, hi = last - base;
+        if (!__builtin_amdgcn_ballot_w64(lo > 0)) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int off = 8 * (e >> 2) + (e & 3);
+                x[e] = off <= hi ? x[e] : -INFINITY;
+            }
+        } else {
+            const uint32_t w = (uint32_t)(hi - lo);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int off = 8 * (e >> 2) + (e & 3);
+                x[e] = (hi >= lo && (uint32_t)(off - lo) <= w) ? x[e] : -INFINITY;
+            }
+        }
+    }
+
     // Stream rows r0 .. r0 + NR - 1 of the [S, D] head at h into the LDS
     // tile at byte address slot, with the given swizzle (blocks wave,
     // wave + NW, ... of its 1 KiB DMA blocks are this wave's). Rows past S
@@ -266,14 +291,8 @@ struct Bwd {
                 float x[16];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) x[e] = fmaf(sa[e], c2, -lse2);
-                if (!full) {
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int j = t * BN + 32 * sb + 8 * (e >> 2) + 4 * g + (e & 3);
-                        const bool ok = j < S && j >= qi - p.win_lo && j <= qi + p.win_hi;
-                        x[e] = ok ? x[e] : -INFINITY;
-                    }
-                }
+                if (!full) mask_block(x, t * BN + 32 * sb + 4 * g, qi - p.win_lo,
+                                      min(qi + p.win_hi, S - 1));
                 uint32_t dsp[8];
 #pragma unroll
                 for (int e = 0; e < 16; e += 2) {
@@ -421,14 +440,8 @@ struct Bwd {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) x[4 * a + w] = fmaf(sa[4 * a + w], c2, -l4[w]);
             }
-            if (!full) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int i = u * QB + 8 * (e >> 2) + 4 * g + (e & 3);
-                    const bool ok = i < S && kj < S && kj >= i - p.win_lo && kj <= i + p.win_hi;
-                    x[e] = ok ? x[e] : -INFINITY;
-                }
-            }
+            if (!full) mask_block(x, u * QB + 4 * g, kj - p.win_hi,
+                                  kj < S ? min(kj + p.win_lo, S - 1) : -1);
             uint32_t pp[8], dsp[8];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
