@@ -646,23 +646,39 @@ struct Kernel {
             __builtin_amdgcn_s_barrier();
         }
 
+        // Group 0's share of the K DMA of step i without MFMAs.
+        __device__ __forceinline__ void dma_k(int i) const {
+            const TileSrc kt = ksrc(i);
+#pragma unroll
+            for (int b = 0; b < G::DMA_PER_WAVE; ++b) dma_block(kt, ad.kdma[b], wave, b);
+        }
         template <int GRP>
         __device__ __forceinline__ void go(State &st) const {
             f32x16 sacc[NKB];
             uint32_t pk[NKB][8];
             const int nt = ntiles;  // >= 1
+            // The last tile (relative) with a key visible to this wave's rows:
+            // past it, M_i and V_i have nothing to do for the wave.
+            const int last = min(S - 1, rlast + win_hi) / BN - t_first;
             if (GRP == 0) {
                 mphase<true, false, true>(st, sacc, pk, 0);
                 vphase<false>(st, sacc, pk, 0);
                 end_step();
-                for (int i = 1; i < nt; ++i) {
+                const int i_end = min(nt, last + 2);
+                int i = 1;
+                for (; i < i_end; ++i) {
                     dma_q_next(i);
                     mphase<true, true, true>(st, sacc, pk, i);
                     vphase<false>(st, sacc, pk, i);
                     end_step();
                 }
+                for (; i < nt; ++i) {  // tiles hidden from the wave: its DMA only
+                    dma_q_next(i);
+                    dma_k(i);
+                    end_step();
+                }
                 dma_q_next(nt);
-                mphase<false, true, false>(st, sacc, pk, nt);
+                if (nt - 1 <= last) mphase<false, true, false>(st, sacc, pk, nt);
                 end_step();
             } else {
                 load_tile(vsrc(0), ad.vdma, wave);
@@ -676,7 +692,7 @@ struct Kernel {
                 }
                 dma_q_next(nt);
                 vphase<false>(st, sacc, pk, nt - 1);
-                mphase<false, true, false>(st, sacc, pk, nt);
+                if (nt - 1 <= last) mphase<false, true, false>(st, sacc, pk, nt);
                 end_step();
             }
         }
