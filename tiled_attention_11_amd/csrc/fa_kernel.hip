@@ -489,6 +489,55 @@ struct Kernel {
         return (2 + (i & 1)) * G::TILE_BYTES;
     }
 
+    // The epilogue of an item for one wave: O = O_acc / l (rounded to the
+    // element type), LSE = ln 2 * (m + log2 l).
+    static __device__ __forceinline__ void store_output(const FwdParams &p, const State &st,
+                                                        int64_t head, int bh, int qi, int S,
+                                                        int rse, int g) {
+        const float l_tot = sum_with_partner(st.l_run);
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        // Elements 4a .. 4a + 3 of block db hold dims 32db + 8a + 4g + 0..3 of
+        // the row, which lanes l and l ^ 32 share. For each pair of 8-dim
+        // chunks (2c, 2c + 1) the two lanes trade halves (v_permlane32_swap
+        // trades lanes 32-63 of its first operand with lanes 0-31 of its
+        // second), so that lane half g holds chunk 2c + g whole and stores it
+        // with one 16-byte write: 32 contiguous bytes of a row per pair of
+        // lanes instead of 16 (the O stores otherwise stall the epilogue).
+        u32x4 ow[NDB][2];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const f32x16 &a = st.oacc[db];
+                const int e0 = 8 * c, e1 = 8 * c + 4;  // chunks 2c and 2c + 1
+                const uint32_t x00 = Elem<T>::pack(a[e0 + 0] * inv, a[e0 + 1] * inv);
+                const uint32_t x01 = Elem<T>::pack(a[e0 + 2] * inv, a[e0 + 3] * inv);
+                const uint32_t x10 = Elem<T>::pack(a[e1 + 0] * inv, a[e1 + 1] * inv);
+                const uint32_t x11 = Elem<T>::pack(a[e1 + 2] * inv, a[e1 + 3] * inv);
+                const auto r0 = __builtin_amdgcn_permlane32_swap(x00, x10, false, false);
+                const auto r1 = __builtin_amdgcn_permlane32_swap(x01, x11, false, false);
+                ow[db][c] = u32x4{(uint32_t)r0[0], (uint32_t)r1[0], (uint32_t)r0[1],
+                                  (uint32_t)r1[1]};
+            }
+        if (qi < S) {
+            uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * rse;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    *reinterpret_cast<u32x4 *>(orow + 32 * db + 16 * c + 8 * g) = ow[db][c];
+            if (p.lse && g == 0) {
+                const float lse = l_tot > 0.0f
+                                      ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
+                                      : -INFINITY;
+                if (PACKED)
+                    p.lse[head / D + (int64_t)qi * p.H] = lse;
+                else
+                    p.lse[(int64_t)bh * S + qi] = lse;
+            }
+        }
+    }
+
     // The key loop of one wave: steps 0 .. T (T tiles), each ended by a
     // workgroup barrier. In step i group 0 runs M_i then V_i, group 1 runs
     // V_(i-1) then M_i, so on each SIMD the two waves' MFMA and softmax phases
@@ -510,6 +559,8 @@ struct Kernel {
         const Addr &ad;
         int kbase;             // slot parity of this item's tile 0
         const Item &nx;        // the workgroup's next item (nx.nt == 0: none)
+        int64_t head;          // element offset of row 0 of the item's head
+        int bh;
 
         __device__ __forceinline__ bool tile_full(int t) const {
             const int k0 = t * BN;
@@ -652,8 +703,11 @@ struct Kernel {
 #pragma unroll
             for (int b = 0; b < G::DMA_PER_WAVE; ++b) dma_block(kt, ad.kdma[b], wave, b);
         }
+        // Returns true when the wave has already stored its output (group 0
+        // does so in the first step whose tiles its rows cannot see, where it
+        // has no other work, instead of at the item boundary).
         template <int GRP>
-        __device__ __forceinline__ void go(State &st) const {
+        __device__ __forceinline__ bool go(State &st) const {
             f32x16 sacc[NKB];
             uint32_t pk[NKB][8];
             const int nt = ntiles;  // >= 1
@@ -672,7 +726,12 @@ struct Kernel {
                     vphase<false>(st, sacc, pk, i);
                     end_step();
                 }
+                bool stored = false;
                 for (; i < nt; ++i) {  // tiles hidden from the wave: its DMA only
+                    if (D == 128 && !stored) {  // (D = 64 has no registers to spare here)
+                        store_output(p, st, head, bh, qi, S, rse, g);
+                        stored = true;
+                    }
                     dma_q_next(i);
                     dma_k(i);
                     end_step();
@@ -680,6 +739,7 @@ struct Kernel {
                 dma_q_next(nt);
                 if (nt - 1 <= last) mphase<false, true, false>(st, sacc, pk, nt);
                 end_step();
+                return stored;
             } else {
                 load_tile(vsrc(0), ad.vdma, wave);
                 mphase<true, false, false>(st, sacc, pk, 0);
@@ -694,6 +754,7 @@ struct Kernel {
                 vphase<false>(st, sacc, pk, nt - 1);
                 if (nt - 1 <= last) mphase<false, true, false>(st, sacc, pk, nt);
                 end_step();
+                return false;
             }
         }
     };
@@ -784,55 +845,10 @@ struct Kernel {
 
             Loop loop{p,     smem,   smem_addr, kh, vh,   S,  S_all,  rse, it.t_first, it.nt,
                       it.t_in_lo, it.t_in_hi, r0, rlast, qi, win_lo, win_hi, c2,  g, wave,
-                      lane,  ad,     kbase,     nx};
-            if (grp == 0)
-                loop.template go<0>(st);
-            else
-                loop.template go<1>(st);
+                      lane,  ad,     kbase,     nx,   head, it.bh};
+            const bool stored = grp == 0 ? loop.template go<0>(st) : loop.template go<1>(st);
 
-            // ---- epilogue: O = O_acc / l, LSE = ln 2 * (m + log2 l) ----
-            const float l_tot = sum_with_partner(st.l_run);
-            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-            // Elements 4a .. 4a + 3 of block db hold dims 32db + 8a + 4g + 0..3 of
-            // the row, which lanes l and l ^ 32 share. For each pair of 8-dim
-            // chunks (2c, 2c + 1) the two lanes trade halves (v_permlane32_swap
-            // trades lanes 32-63 of its first operand with lanes 0-31 of its
-            // second), so that lane half g holds chunk 2c + g whole and stores it
-            // with one 16-byte write: 32 contiguous bytes of a row per pair of
-            // lanes instead of 16 (the O stores otherwise stall the epilogue).
-            u32x4 ow[NDB][2];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const f32x16 &a = st.oacc[db];
-                    const int e0 = 8 * c, e1 = 8 * c + 4;  // chunks 2c and 2c + 1
-                    const uint32_t x00 = Elem<T>::pack(a[e0 + 0] * inv, a[e0 + 1] * inv);
-                    const uint32_t x01 = Elem<T>::pack(a[e0 + 2] * inv, a[e0 + 3] * inv);
-                    const uint32_t x10 = Elem<T>::pack(a[e1 + 0] * inv, a[e1 + 1] * inv);
-                    const uint32_t x11 = Elem<T>::pack(a[e1 + 2] * inv, a[e1 + 3] * inv);
-                    const auto r0 = __builtin_amdgcn_permlane32_swap(x00, x10, false, false);
-                    const auto r1 = __builtin_amdgcn_permlane32_swap(x01, x11, false, false);
-                    ow[db][c] = u32x4{(uint32_t)r0[0], (uint32_t)r1[0], (uint32_t)r0[1],
-                                      (uint32_t)r1[1]};
-                }
-            if (qi < S) {
-                uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * rse;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        *reinterpret_cast<u32x4 *>(orow + 32 * db + 16 * c + 8 * g) = ow[db][c];
-                if (p.lse && g == 0) {
-                    const float lse = l_tot > 0.0f
-                                          ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
-                                          : -INFINITY;
-                    if (PACKED)
-                        p.lse[head / D + (int64_t)qi * p.H] = lse;
-                    else
-                        p.lse[(int64_t)it.bh * S + qi] = lse;
-                }
-            }
+            if (!stored) store_output(p, st, head, it.bh, qi, S, rse, g);
             kbase += it.nt;
             it = nx;
         }
