@@ -752,11 +752,22 @@ struct Kernel {
                 end_step();
                 return stored;
             } else {
+                // The first tile (relative) with a key visible to this wave's
+                // rows: before it, M_i has nothing to do for the wave (V_i takes
+                // its fast path for a hidden tile and still streams its DMA).
+                const int first = min(nt, max(0, r0 - win_lo) / BN - t_first);
                 load_tile(vsrc(0), ad.vdma, wave);
                 mid_step();
-                mphase<true, false, false>(st, sacc, pk, 0);
+                if (first == 0) mphase<true, false, false>(st, sacc, pk, 0);
                 end_step();
-                for (int i = 1; i < nt; ++i) {
+                int i = 1;
+                for (; i < first; ++i) {
+                    dma_q_next(i);
+                    vphase<true>(st, sacc, pk, i - 1);
+                    mid_step();
+                    end_step();
+                }
+                for (; i < nt; ++i) {
                     dma_q_next(i);
                     vphase<true>(st, sacc, pk, i - 1);
                     mid_step();
