@@ -81,6 +81,20 @@ def _inputs(name):
     return _CACHE[key]
 
 
+# More query tiles than workgroups: each workgroup runs several items back to
+# back, so the next item's Q and K(0) prefetch, the per-wave skipped leading
+# and trailing steps and the early output stores all meet whole-tensor parity.
+@pytest.mark.parametrize("shape", [(4, 64, 512, 128), (2, 64, 640, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("mask,window", [("causal", (-1, -1)), ("window", (100, 0)),
+                                         ("window", (37, 50))], ids=str)
+def test_parity_many_items_per_workgroup(orc, shape, mask, window):
+    B, H, S, D = shape
+    say("many items", shape, mask, window)
+    q, k, v = synth.make_qkv(B, H, S, D, "f16", 93)
+    check_full(orc, q, k, v, "f16", 1.0 / math.sqrt(D), mask, window)
+
+
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_parity_workload(orc, name):
     w = synth.WORKLOADS[name]
