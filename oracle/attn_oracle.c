@@ -674,7 +674,11 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
                 for (int64_t j = 0; j < S; ++j) {
                     if (Pi[j] == 0.0) continue;          /* hidden (or underflowed) pair */
                     g += dSi[j] * kd[j * D + d];
+#if ORACLE_PLANT == 12
+                    mg += fmax(fabs(dSi[j]), tiny) * fabs(kd[j * D + d]);  /* planted: no P A term */
+#else
                     mg += (fmax(fabs(dSi[j]), tiny) + Pi[j] * a) * fabs(kd[j * D + d]);
+#endif
                 }
                 dq[base + i * D + d] = scale * g;
                 mag_dq[base + i * D + d] = fabs(scale) * mg;
@@ -694,7 +698,11 @@ int oracle_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v
                     mk += (fmax(fabs(ds), tiny) + p * A[i]) * fabs(qd[i * D + d]);
                 }
                 dv[base + j * D + d] = gv;
+#if ORACLE_PLANT == 11
+                mag_dv[base + j * D + d] = 2.0 * mv;     /* planted: doubled sum */
+#else
                 mag_dv[base + j * D + d] = mv;
+#endif
                 dk[base + j * D + d] = scale * gk;
                 mag_dk[base + j * D + d] = fabs(scale) * mk;
             }

@@ -564,6 +564,42 @@ def pin_bwd_autograd(orc):
                     assert np.all(np.abs(g) <= m * (1 + 1e-12) + 1e-300)
 
 
+def pin_bwd_magnitude_sums(orc):
+    """The magnitude sums that set the backward comparison rule, evaluated
+    independently: P from torch's softmax of the masked fp64 scores, dS as
+    torch autograd's gradient of the loss sum(O * dO) with respect to the
+    scaled-score matrix, A_i = sum_d |dO_id O_id| with O = P V, and the three
+    sums as numpy matrix products over the visible pairs, each operand of a
+    rounded product (P, dS) floored at the element type's smallest normal:
+      mag_dV = (max(P, t) on visible pairs)^T |dO|,
+      mag_dQ = |scale| (max(|dS|, t) + P A) |K|,   mag_dK = |scale| (...)^T |Q|."""
+    rng = np.random.default_rng(44)
+    for dtype, tiny in (("f16", 2.0 ** -14), ("bf16", 2.0 ** -126)):
+        for S, scale in ((1, 0.45), (11, 0.45), (29, -0.8)):
+            q, k, v = make_qkv(1, 2, S, 8, dtype, seed=int(rng.integers(1 << 30)))
+            do, _, _ = make_qkv(1, 2, S, 8, dtype, seed=int(rng.integers(1 << 30)))
+            Q, K, V, dO = (_decode_ref(x, dtype) for x in (q, k, v, do))
+            for mask, window in MASK_CASES:
+                vis = _bool_mask_kv(S, S, mask, window)
+                _, mags = orc.attention_bwd(q, k, v, do, dtype, scale, mask, window)
+                for h in range(2):
+                    s = torch.from_numpy(Q[0, h] @ K[0, h].T * scale).requires_grad_(True)
+                    P = torch.softmax(s.masked_fill(~torch.from_numpy(vis), -math.inf), dim=1)
+                    O = P @ torch.from_numpy(V[0, h])
+                    (O * torch.from_numpy(dO[0, h])).sum().backward()
+                    Pn = P.detach().numpy()
+                    dS = s.grad.numpy()
+                    A = np.abs(dO[0, h] * O.detach().numpy()).sum(axis=1)
+                    wv = np.where(vis, np.maximum(Pn, tiny), 0.0)
+                    wqk = np.where(vis, np.maximum(np.abs(dS), tiny) + Pn * A[:, None], 0.0)
+                    ref_dv = wv.T @ np.abs(dO[0, h])
+                    ref_dq = abs(scale) * (wqk @ np.abs(K[0, h]))
+                    ref_dk = abs(scale) * (wqk.T @ np.abs(Q[0, h]))
+                    for got, ref in zip(mags, (ref_dq, ref_dk, ref_dv)):
+                        assert np.allclose(got[0, h], ref, rtol=1e-10, atol=1e-300), \
+                            (dtype, S, mask, window, h)
+
+
 def pin_bwd_closed_forms(orc):
     """Q = 0 (uniform weights): dV_j is the sum over the rows that see key j of
     dO_i divided by their visible-key count, and dK = 0 when V rows are all
@@ -677,5 +713,6 @@ ALL_PINS = [
     pin_rope_zero_angle_is_plain_attention,
     pin_bwd_autograd,
     pin_bwd_closed_forms,
+    pin_bwd_magnitude_sums,
     pin_kv_rope_is_the_tail_of_the_square_case,
 ]
