@@ -56,6 +56,41 @@ def test_parity_whole_tensor(orc, dtype, shape, mask, window):
     check_full(orc, q, k, v, dtype, 1.0 / math.sqrt(D), mask, window)
 
 
+# Work layouts: grids of fewer than two 256-row items per CU run the key-split
+# variant (128-row items, the two wave groups on alternate key tiles, merged at
+# the end); many heads at a short length keep the 256-row items. Both layouts
+# meet every mask and both head dimensions here (the small whole-tensor shapes
+# above and the tail cases are key-split launches).
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(8, 64, 300, 128), (4, 128, 200, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("mask,window", [("full", (-1, -1)), ("causal", (-1, -1)),
+                                         ("window", (-1, 20)), ("window", (299, 3))], ids=str)
+def test_parity_unsplit_layout(orc, dtype, shape, mask, window):
+    B, H, S, D = shape
+    say("unsplit layout", dtype, shape, mask, window)
+    q, k, v = synth.make_qkv(B, H, S, D, dtype, seed=200 + S + D)
+    check_full(orc, q, k, v, dtype, 1.0 / math.sqrt(D), mask, window)
+
+
+# The key-split layout at item counts that exercise its edges: one key tile per
+# item (the odd group has none), odd tile counts, an item whose last rows lie
+# past the sequence, several items per workgroup, windows that leave a group
+# without visible tiles for some waves.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 2, 40, 128), (1, 3, 64, 64), (2, 3, 129, 128),
+                                   (1, 2, 448, 64), (2, 64, 700, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("mask,window", [("causal", (-1, -1)), ("window", (0, 0)),
+                                         ("window", (63, 0)), ("window", (130, 70)),
+                                         ("full", (-1, -1))], ids=str)
+def test_parity_split_layout_edges(orc, dtype, shape, mask, window):
+    B, H, S, D = shape
+    say("split layout", dtype, shape, mask, window)
+    q, k, v = synth.make_qkv(B, H, S, D, dtype, seed=300 + S + D)
+    check_full(orc, q, k, v, dtype, 1.0 / math.sqrt(D), mask, window)
+
+
 @pytest.mark.parametrize("S", [1, 2, 31, 63, 64, 65, 127, 128, 129, 200, 1000])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("mask,window", [("causal", (-1, -1)), ("full", (-1, -1)),
@@ -95,21 +130,113 @@ def test_parity_many_items_per_workgroup(orc, shape, mask, window):
     check_full(orc, q, k, v, "f16", 1.0 / math.sqrt(D), mask, window)
 
 
-@pytest.mark.parametrize("name", list(synth.WORKLOADS))
-def test_parity_workload(orc, name):
+# Named workloads checked over the whole tensor, head chunk by head chunk (a
+# chunk's oracle rows take about 15 s on 16 host cores at the B4 H32 S4096
+# D128 causal shape), and those checked on at least 32k rows that include
+# every head's query-tile, key-tile and window edges.
+WHOLE = ("tiny_full", "tiny_causal", "d64_causal", "b4h32s4096_causal",
+         "b4h32s4096_win1024", "b4h32s4096_win1000")
+SAMPLED = ("b4h32s4096_full", "long_bf16_outliers", "b4h32s4096_causal_rope")
+HEADS_PER_CHUNK = 16
+_OUT = {}
+
+
+def _workload_output(name):
+    """The GPU result of a named workload, in the launch the benchmark times
+    (computed once per workload; RoPE workloads through forward_rope)."""
+    if name not in _OUT:
+        _OUT.clear()
+        w = synth.WORKLOADS[name]
+        q, k, v = _inputs(name)
+        if w.get("rope"):
+            cos, sin = synth.rope_tables(w["S"], w["D"], w["rope_base"])
+            tq, tk, tv = (to_device(x, w["dtype"]) for x in (q, k, v))
+            o, lse, _ = fa.forward_rope(tq, tk, tv, torch.from_numpy(cos).cuda(),
+                                        torch.from_numpy(sin).cuda(), mode=w["rope"],
+                                        scale=w["scale"], mask=w["mask"], window=w["window"])
+            torch.cuda.synchronize()
+            _OUT[name] = (to_bits(o), lse.cpu().numpy(), (cos, sin))
+        else:
+            o_bits, lse = gpu_run(q, k, v, w["dtype"], w["scale"], w["mask"], w["window"])
+            _OUT[name] = (o_bits, lse, None)
+    return _OUT[name]
+
+
+def _oracle_rows(orc, name, rows):
+    w = synth.WORKLOADS[name]
+    q, k, v = _inputs(name)
+    if w.get("rope"):
+        cos, sin = _workload_output(name)[2]
+        return orc.attention_rope_rows(q, k, v, w["dtype"], w["scale"], w["mask"], w["window"],
+                                       cos, sin, w["rope"], rows=rows)
+    return orc.attention_rows(q, k, v, w["dtype"], w["scale"], w["mask"], w["window"], rows)
+
+
+def _chunks():
+    out = []
+    for name in WHOLE:
+        w = synth.WORKLOADS[name]
+        bh = w["B"] * w["H"]
+        for c0 in range(0, bh, HEADS_PER_CHUNK):
+            out.append((name, c0, min(bh, c0 + HEADS_PER_CHUNK)))
+    return out
+
+
+@pytest.mark.parametrize("name,h0,h1", _chunks(), ids=lambda x: str(x))
+def test_parity_workload_whole(orc, name, h0, h1):
+    """Every row of heads h0 .. h1-1 of a named workload at full size."""
     w = synth.WORKLOADS[name]
     B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
-    say("workload", name, (B, H, S, D), dtype, w["mask"], w["window"], "seed", w["seed"])
-    q, k, v = _inputs(name)
-    o_bits, lse = gpu_run(q, k, v, dtype, w["scale"], w["mask"], w["window"])
-    wl = w["window"][0]
-    extra = (wl - 1, wl, wl + 1, wl + 63, wl + 64) if wl > 0 else ()
-    rows = sample_rows(B, H, S, 1024 if B * H * S > 65536 else B * H * S, seed=w["seed"],
-                       extra_i=extra)
-    o_ref, lse_ref = orc.attention_rows(q, k, v, dtype, w["scale"], w["mask"], w["window"], rows)
+    say("workload whole", name, (B, H, S, D), dtype, w["mask"], w["window"], "seed", w["seed"],
+        "heads", h0, h1)
+    o_bits, lse, _ = _workload_output(name)
+    rows = np.arange(h0 * S, h1 * S, dtype=np.int64)
+    o_ref, lse_ref = _oracle_rows(orc, name, rows)
     st = compare(o_bits.reshape(-1, D)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, dtype)
     say("stats", st)
     assert st["pass"], st
+
+
+def edge_rows(B, H, S, n_min, seed, extra_i=()):
+    """Flat row indices: for every head the rows at query-tile (256), key-tile
+    (64) and wave (32) edges near both ends and the middle of the sequence,
+    plus the ``extra_i`` positions (window edges), topped up with random rows
+    to at least ``n_min``."""
+    edges = set()
+    for c in (0, 256, S // 2, S - 256):
+        for o in (0, 1, 31, 32, 63, 64, 65, 127, 128, 255):
+            edges.add(c + o)
+            edges.add(c - 1 - o)
+    edges.update((S - 1, S - 2, *extra_i))
+    edges = np.array(sorted(i for i in edges if 0 <= i < S), dtype=np.int64)
+    rows = (np.arange(B * H, dtype=np.int64)[:, None] * S + edges[None, :]).ravel()
+    rng = np.random.default_rng(seed)
+    need = max(0, n_min - rows.size)
+    if need:
+        rows = np.concatenate([rows, rng.choice(B * H * S, size=need + rows.size, replace=False)])
+    rows = np.unique(rows)
+    return rows
+
+
+@pytest.mark.parametrize("name", SAMPLED)
+def test_parity_workload_sampled(orc, name):
+    """A named workload at full size on >= 32k rows including every head's edges."""
+    w = synth.WORKLOADS[name]
+    B, H, S, D, dtype = w["B"], w["H"], w["S"], w["D"], w["dtype"]
+    say("workload sampled", name, (B, H, S, D), dtype, w["mask"], w["window"], "seed", w["seed"])
+    o_bits, lse, _ = _workload_output(name)
+    wl = w["window"][0]
+    extra = (wl - 1, wl, wl + 1, wl + 63, wl + 64) if wl > 0 else ()
+    rows = edge_rows(B, H, S, 32768, seed=w["seed"], extra_i=extra)
+    assert rows.size >= 32768
+    o_ref, lse_ref = _oracle_rows(orc, name, rows)
+    st = compare(o_bits.reshape(-1, D)[rows], lse.reshape(-1)[rows], o_ref, lse_ref, dtype)
+    say("stats", st)
+    assert st["pass"], st
+
+
+def test_named_workloads_are_all_covered():
+    assert set(WHOLE) | set(SAMPLED) == set(synth.WORKLOADS)
 
 
 # ---------------------------------------------------------------------------

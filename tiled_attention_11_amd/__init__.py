@@ -6,9 +6,10 @@ A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
 ``fa_bwd_workspace_bytes``, ``fa_bwd_flops``, ``fa_decode``, ``fa_decode_rope``,
 ``fa_decode_paged_rope``,
 ``fa_decode_workspace_bytes``, ``fa_decode_flops``, ``fa_decode_paged``,
-``fa_decode_paged_workspace_bytes`` and ``fa_strerror`` carry the C names and
-arguments (marshalling only). ``forward``, ``forward_varlen``, ``rope``,
-``forward_rope``, ``backward``, ``decode`` and ``decode_paged`` are the convenience entries
+``fa_decode_paged_workspace_bytes`` and ``fa_strerror``
+carry the C names and arguments (marshalling only). ``forward``,
+``forward_varlen``, ``rope``, ``forward_rope``, ``backward``, ``decode``
+and ``decode_paged`` are the convenience entries
 for torch tensors: torch supplies device memory and the stream; every step of
 the computation runs in the library's HIP kernels.
 There is no fallback: if the library is missing, importing this package
@@ -24,9 +25,9 @@ __all__ = [
     "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_rope", "fa_fwd_rope", "FA_ROPE_HALVES",
     "FA_ROPE_INTERLEAVED", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_flops", "fa_decode",
     "fa_decode_rope", "fa_decode_paged_rope", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
-    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward", "forward_varlen", "rope", "forward_rope", "backward", "decode",
-    "decode_paged",
-    "lib_path", "library",
+    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward",
+    "forward_varlen", "rope", "forward_rope", "backward", "decode",
+    "decode_paged", "lib_path", "library", "load_library",
 ]
 
 FA_MASK_FULL, FA_MASK_CAUSAL, FA_MASK_WINDOW = 0, 1, 2
@@ -42,7 +43,7 @@ def lib_path():
     return os.environ.get("FA_LIBRARY", os.path.join(_HERE, "libfa.so"))
 
 
-def _load():
+def _load(path=None):
     # torch ships its own HIP runtime (SONAME libamdhip64.so.7). Loading torch
     # first makes libfa bind to that same runtime instead of pulling a second
     # copy from /opt/rocm, so torch's streams and pointers stay valid in libfa.
@@ -50,7 +51,7 @@ def _load():
         import torch  # noqa: F401
     except ImportError:
         pass
-    path = lib_path()
+    path = path or lib_path()
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is not built; run `python -m tiled_attention_11_amd._build` "
@@ -112,6 +113,13 @@ _lib = _load()
 def library():
     """The loaded ``ctypes.CDLL``."""
     return _lib
+
+
+def load_library(path):
+    """Another build of the same C ABI (e.g. the conservative-sync variant
+    ``libfa_sync.so`` next to ``libfa.so``) as a ``ctypes.CDLL`` with the
+    same argument types."""
+    return _load(path)
 
 
 class FaError(RuntimeError):

@@ -11,6 +11,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
+# The same sources built with FA_CONSERVATIVE_SYNC=1: every DMA and every LDS
+# phase waited for, a barrier between the halves of every key step. It must
+# give bit-identical results (a GPU test compares the two); not used otherwise.
+LIB_SYNC = os.path.join(PKG, "libfa_sync.so")
+SYNC_FLAGS = ("-DFA_CONSERVATIVE_SYNC=1",)
 SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_kernel.hip"),
            os.path.join(CSRC, "fa_decode.hip"), os.path.join(CSRC, "fa_rope.hip"),
            os.path.join(CSRC, "fa_bwd.hip")]
@@ -28,19 +33,36 @@ def command(out=LIB, extra=()):
             + SOURCES + ["-o", out])
 
 
-def build(out=LIB, extra=(), quiet=True):
-    """Compile every source into ``out``; raise with the compiler output on failure."""
+def _start(out, extra):
     tmp = out + ".tmp"
     cmd = command(tmp, extra)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("libfa build failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    return cmd, tmp, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                      text=True)
+
+
+def _finish(job, out, quiet):
+    cmd, tmp, proc = job
+    _, err = proc.communicate()
+    if proc.returncode != 0:
+        raise RuntimeError(f"{os.path.basename(out)} build failed:\n" + " ".join(cmd) + "\n" + err)
     if not quiet:
         noise = "is not a recognized feature for this target"
-        lines = [l for l in res.stderr.splitlines() if noise not in l]
+        lines = [l for l in err.splitlines() if noise not in l]
         if lines:
             print("\n".join(lines))
     os.replace(tmp, out)
+    return out
+
+
+def build(out=LIB, extra=(), quiet=True, sync_variant=True):
+    """Compile every source into ``out`` (and, by default, the conservative-sync
+    variant into libfa_sync.so, in parallel); raise with the compiler output on
+    failure."""
+    jobs = [(_start(out, extra), out)]
+    if sync_variant:
+        jobs.append((_start(LIB_SYNC, tuple(extra) + SYNC_FLAGS), LIB_SYNC))
+    for job, o in jobs:
+        _finish(job, o, quiet)
     return out
 
 

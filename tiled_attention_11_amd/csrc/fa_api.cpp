@@ -8,6 +8,7 @@
 #include "fa_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -60,19 +61,44 @@ float base2_scale(float scale) {
 // Work distribution and launch of the forward kernel, for p with everything
 // but the fields set here filled in: one workgroup per CU (each takes a whole
 // CU), each running its share of the bh * n_qtiles query tiles; see FwdParams.
+// The current device's CU count, queried once per device and cached (a
+// relaxed atomic per device: concurrent first calls store the same value).
 int device_cus(int *n_cu) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices] = {};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *n_cu = c;
+            return FA_OK;
+        }
+    }
+    if (hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         *n_cu <= 0)
         return FA_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(*n_cu, std::memory_order_relaxed);
     return FA_OK;
 }
 
-int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t n_qtiles, int D, int dtype,
-                        hipStream_t stream) {
+// rows: the sequence length that sets the item count (the longest sequence
+// when packed). allow_split: the layout may use the key-split variant.
+int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int dtype,
+                        hipStream_t stream, bool allow_split) {
     int n_cu = 0;
     if (device_cus(&n_cu) != FA_OK) return FA_ERR_HIP;
+    // The key split (128-row items, the two wave groups of a workgroup on
+    // alternate key tiles, merged at the end) for grids with fewer than two
+    // 256-row items per CU: the heaviest causal item then sets the time, and
+    // half-height items pair up evenly (B1 H32 S2048 D64 causal: 34.0 against
+    // 40.9 us). Not for sliding windows, where it measured 8% slower (each
+    // half-height item still pays a first and a last half-step, and the merge).
+    const uint64_t items256 = bh * ((rows + fa::kBlockM - 1) / fa::kBlockM);
+    const bool split = allow_split && items256 < 2 * (uint64_t)n_cu;
+    const int block_m = split ? fa::kBlockMSplit : fa::kBlockM;
+    const uint64_t n_qtiles = (rows + block_m - 1) / block_m;
+    p.key_split = split;
     p.n_qtiles = (int)n_qtiles;
     const uint64_t n_items = bh * n_qtiles;
     uint64_t grid = n_items < (uint64_t)n_cu ? n_items : (uint64_t)n_cu;
@@ -161,7 +187,7 @@ int fwd_core(const void *q, const void *k, const void *v, void *o, float *lse, i
     const uint64_t head_bytes = (uint64_t)S * D * 2;
     if (head_bytes >= (1ull << 31)) return FA_ERR_TOO_LARGE;
     const uint64_t bh = (uint64_t)B * H;
-    const uint64_t n_qtiles = ((uint64_t)S + fa::kBlockM - 1) / fa::kBlockM;
+    const uint64_t n_qtiles = ((uint64_t)S + fa::kBlockMSplit - 1) / fa::kBlockMSplit;
     if (bh * n_qtiles > (uint64_t)INT32_MAX) return FA_ERR_TOO_LARGE;
     const __int128 tensor_bytes = (__int128)bh * head_bytes;
     if (tensor_bytes > (__int128)INT64_MAX / 4) return FA_ERR_TOO_LARGE;
@@ -236,7 +262,7 @@ int fwd_core(const void *q, const void *k, const void *v, void *o, float *lse, i
     p.rope_cos = rope ? rope->cos : nullptr;
     p.rope_sin = rope ? rope->sin : nullptr;
     p.rope_interleaved = rope ? rope->mode == FA_ROPE_INTERLEAVED : 0;
-    return plan_and_launch_fwd(p, bh, n_qtiles, D, dtype, stream);
+    return plan_and_launch_fwd(p, bh, (uint64_t)S, D, dtype, stream, true);
 }
 
 }  // namespace
@@ -352,7 +378,8 @@ extern "C" int fa_fwd_varlen(const void *q, const void *k, const void *v, void *
         const int n = std::min(nseq - first, fa::kMaxPackedSeqs);
         p.B = n;
         p.cu_seqlens = cu_seqlens + first;
-        const int rc = plan_and_launch_fwd(p, (uint64_t)n * H, n_qtiles, D, dtype, stream);
+        const int rc =
+            plan_and_launch_fwd(p, (uint64_t)n * H, (uint64_t)max_seqlen, D, dtype, stream, false);
         if (rc != FA_OK) return rc;
     }
     return FA_OK;
@@ -504,11 +531,8 @@ int plan_decode(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l, i
     }
     // Splits: about two workgroups (one wave each) per CU over all heads,
     // never more than one per tile.
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n_cu <= 0)
-        return FA_ERR_HIP;
+    int n_cu = 0;
+    if (device_cus(&n_cu) != FA_OK) return FA_ERR_HIP;
     const int64_t bh = (int64_t)B * H;
     int64_t want = (2 * (int64_t)n_cu + bh - 1) / bh;
     if (want > nt) want = nt;

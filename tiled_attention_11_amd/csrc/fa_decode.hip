@@ -44,6 +44,7 @@
 #include "fa_internal.h"
 
 namespace fa {
+
 namespace {
 
 using namespace dev;
@@ -244,13 +245,25 @@ struct Decode {
                 for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
             }
             const float mu = (m_run == -INFINITY) ? 0.0f : m_run;
-            uint32_t pk[8];
+            // bf16 keeps only 8 significant bits of each probability, which
+            // moves a short row's output by up to about one bf16 unit before
+            // its own rounding. The cache kernel is bound by HBM, not by the
+            // matrix cores, so for bf16 it also feeds the rounding remainder
+            // p - bf16(p) (itself rounded, 16 bits in all) through a second
+            // product with the same V^T operand.
+            constexpr bool kSplitP = Elem<T>::kCoarse;
+            uint32_t pk[8], pr[8] = {};
             float ps0 = 0.0f, ps1 = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[r], c2, -mu));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[r + 1], c2, -mu));
                 pk[r >> 1] = Elem<T>::pack(p0, p1);
+                if constexpr (kSplitP) {
+                    const float h0 = __builtin_bit_cast(float, pk[r >> 1] << 16);
+                    const float h1 = __builtin_bit_cast(float, pk[r >> 1] & 0xffff0000u);
+                    pr[r >> 1] = Elem<T>::pack(p0 - h0, p1 - h1);
+                }
                 if (Elem<T>::kSumRounded) {
                     ps0 = Elem<T>::sum2(pk[r >> 1], ps0);
                 } else {
@@ -268,6 +281,10 @@ struct Decode {
             for (int c = 0; c < NPC; ++c) {
                 const u32x4 pw = {pk[4 * c + 0], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
                 const vec8 b = __builtin_bit_cast(vec8, pw);
+                vec8 br{};
+                if constexpr (kSplitP)
+                    br = __builtin_bit_cast(vec8, u32x4{pr[4 * c + 0], pr[4 * c + 1],
+                                                        pr[4 * c + 2], pr[4 * c + 3]});
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const LDS char *base = st + vo[db] + 16 * c * G::RB;
@@ -279,11 +296,13 @@ struct Decode {
                     const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
                     const vec8 a = __builtin_bit_cast(vec8, u32x4{l2[0], l2[1], h2[0], h2[1]});
                     oacc[db] = Elem<T>::mma(a, b, oacc[db]);
+                    if constexpr (kSplitP) oacc[db] = Elem<T>::mma(a, br, oacc[db]);
                 }
             }
             // Every LDS read of this stage has returned (the MFMAs consumed
             // them) before the stage is refilled at the next iteration's DMA.
             pin(oacc);
+            conservative_lds_wait();
         }
 
         // ---- this split's result -------------------------------------------

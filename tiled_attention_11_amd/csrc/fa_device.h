@@ -16,6 +16,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -32,10 +33,13 @@ template <typename T> struct Elem;
 template <> struct Elem<_Float16> {
     typedef f16x8 vec8;
     typedef f16x2 vec2;
-    // The row sum adds the fp16-rounded probabilities (the P V operands), two
-    // per v_dot2 against (1, 1), in the MFMA phase; their rounding (relative
-    // 2^-12 at most) moves the LSE by under 2.5e-4.
+    // The cache kernel's row sum adds the fp16-rounded probabilities (the
+    // P V operands), two per v_dot2 against (1, 1); their rounding (relative
+    // 2^-12 at most) moves the LSE by under 2.5e-4. (The prefill forward sums
+    // the unrounded fp32 probabilities for both types.)
     static constexpr bool kSumRounded = true;
+    // 8 significant bits: the cache kernel feeds P to its product in two parts.
+    static constexpr bool kCoarse = false;
     // acc + a.lo + a.hi for two packed fp16 values
     static __device__ __forceinline__ float sum2(uint32_t a, float acc) {
         const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
@@ -54,8 +58,9 @@ template <> struct Elem<__bf16> {
     typedef bf16x8 vec8;
     typedef bf16x2 vec2;
     // bf16 rounding (relative 2^-9) would move the LSE by up to 2e-3: the row
-    // sum adds the unrounded fp32 probabilities in the softmax instead.
+    // sum adds the unrounded fp32 probabilities instead.
     static constexpr bool kSumRounded = false;
+    static constexpr bool kCoarse = true;
     static __device__ __forceinline__ float sum2(uint32_t, float acc) { return acc; }
     static __device__ __forceinline__ f32x16 mma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -78,6 +83,31 @@ template <int D> __device__ __forceinline__ int kchunk(int q, int r) {
 // segments.
 template <int D> __device__ __forceinline__ int vchunk(int q, int r) {
     return D == 128 ? (q ^ ((r & 3) << 2)) : (q ^ (((r >> 1) & 1) << 2));
+}
+
+// ---- conservative synchronisation (a checking build) ----------------------------
+// Compiled with FA_CONSERVATIVE_SYNC=1 the kernels wait for every DMA right
+// after issuing it (vmcnt 0), wait for every LDS read at the end of every phase
+// (lgkmcnt 0) and put a fenced workgroup barrier between the two halves of
+// every step of the forward's key loop. The arithmetic is unchanged, so that
+// build must give bit-identical results: a test compares it with the release
+// build, which orders its DMA and LDS traffic by hand.
+#ifndef FA_CONSERVATIVE_SYNC
+#define FA_CONSERVATIVE_SYNC 0
+#endif
+constexpr bool kConservativeSync = FA_CONSERVATIVE_SYNC != 0;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): wait for all vector-memory operations, or for all LDS ones.
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (3 << 14);
+
+__device__ __forceinline__ void conservative_lds_wait() {
+    if constexpr (kConservativeSync) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        asm volatile("" ::: "memory");
+    }
 }
 
 // ---- HBM -> LDS DMA ---------------------------------------------------------
@@ -106,6 +136,10 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t vo
         : "=&s"(saved)
         : "s"(lds_base), "v"(voffset), "s"(rsrc)
         : "memory");
+    if constexpr (kConservativeSync) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        asm volatile("" ::: "memory");
+    }
 }
 
 // ---- wave-level helpers ------------------------------------------------------
@@ -123,6 +157,17 @@ template <int N, int M> __device__ __forceinline__ void pin(uint32_t (&x)[N][M])
     for (int n = 0; n < N; ++n)
 #pragma unroll
         for (int m = 0; m < M; ++m) asm volatile("" : "+v"(x[n][m]));
+}
+
+// A workgroup barrier that is also a compiler memory fence: the compiler
+// models s_barrier as touching no memory, so without the empty asm clobbers it
+// could move an LDS read of the next step above the barrier (and past the
+// refill of the slot it reads) or a DMA issue of this step below it. Costs no
+// instruction.
+__device__ __forceinline__ void fence_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float max_with_partner(float x) {

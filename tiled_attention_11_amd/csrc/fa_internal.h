@@ -51,6 +51,10 @@ struct FwdParams {
     // pairs of halves or (rope_interleaved) of neighbours. k is read as given.
     const float *rope_cos, *rope_sin;
     int rope_interleaved;
+    // Key split ([B, H, S, D] only): work items of kBlockMSplit rows whose two
+    // wave groups take alternate key tiles and merge at the end (n_qtiles then
+    // counts items of that height).
+    int key_split;
 };
 
 // Rotary embedding of x [rows / S, S, D] into y (may be x): row r at position r % S.
@@ -65,8 +69,9 @@ struct RopeParams {
 
 hipError_t launch_rope(const RopeParams &p, int D, int dtype, hipStream_t stream);
 
-// Query rows per workgroup of every kernel variant.
+// Query rows per work item of the forward kernel, and of its key-split variant.
 constexpr int kBlockM = 256;
+constexpr int kBlockMSplit = 128;
 // Sequences of one packed launch (the kernel keeps a table of them in LDS);
 // the host splits larger batches over several launches.
 constexpr int kMaxPackedSeqs = 1024;

@@ -86,15 +86,35 @@ template <int D> struct Geom {
 // PACKED: rows of a head lie H * D elements apart in packed [T, H, D] tensors
 // of variable-length sequences (FwdParams row addressing); otherwise [B, H, S, D].
 // ROPE: query rows get their rotary embedding as they are read (FwdParams).
-template <typename T, int D, bool PACKED, bool ROPE>
+// KS (key split): a work item is kBlockMSplit = 128 query rows; waves w and
+// w + 4 own the same 32 rows and take alternate key tiles (group 0 the even
+// tiles of the item's range, group 1 the odd ones), each with its own online
+// softmax state, merged through LDS at the end of the item. Items are half as
+// tall, so a window (or a short causal row block) wastes fewer masked pairs and
+// a small grid has twice as many items to balance; the price is the merge and
+// twice the K/V tile traffic into LDS per step. Not combined with PACKED (the
+// layout fills all 160 KiB of LDS).
+template <typename T, int D, bool PACKED, bool ROPE, bool KS>
 struct Kernel {
     typedef Geom<D> G;
     typedef typename Elem<T>::vec8 vec8;
+    static_assert(!(KS && PACKED), "the key-split layout leaves no LDS for the sequence table");
+    static constexpr int BM = KS ? kBlockMSplit : kBlockM;  // query rows per item
     static constexpr int BN = G::BN;
     static constexpr int NKB = BN / 32;   // 32-key score blocks per tile
     static constexpr int NDC = D / 16;    // 16-dim chunks of the QK^T contraction
     static constexpr int NDB = D / 32;    // 32-dim output blocks
     static constexpr int NPC = BN / 16;   // 16-key chunks of the PV contraction
+    // The probabilities as MFMA operands: per 32-key block, 8 dwords of pairs
+    // rounded to the element type, and for bf16 (8 significant bits) 8 more
+    // holding the rounding remainders p - bf16(p), themselves rounded, which a
+    // second product with the same V^T operand adds: 16 bits of each
+    // probability reach the output. (One bf16 product alone leaves errors of
+    // up to 2^-9 of sum_j p_j |v_j| / l, several output ulps where two large
+    // terms cancel.)
+    static constexpr bool kSplitP = Elem<T>::kCoarse;
+    static constexpr int NPW = kSplitP ? 16 : 8;
+    typedef uint32_t PBuf[NKB][NPW];
 
     // Per-wave state carried across key tiles.
     struct State {
@@ -180,7 +200,7 @@ struct Kernel {
     }
 
     // ---- work items -------------------------------------------------------------
-    // A work item is one query tile (kBlockM rows) of one (b, h). The grid has
+    // A work item is one query tile (BM rows) of one (b, h). The grid has
     // at most one workgroup per CU and workgroup w runs its items r = 0, 1, ...
     // back to back as one stream of key tiles. Items are laid out in lists:
     // with B*H a multiple of 8, list x holds the heads x, x + 8, x + 16, ... and
@@ -241,7 +261,7 @@ struct Kernel {
         const int qt = nq - 1 - within / gh;
         const int hl = grp * gh + within % gh;
         it.bh = p.xcd_lists ? hl * 8 + x : hl;
-        it.q0 = qt * kBlockM;
+        it.q0 = qt * BM;
         finish_item(p, it, p.S);
         return it;
     }
@@ -265,7 +285,7 @@ struct Kernel {
         const int lane = threadIdx.x & 63;
         int total = 0;
         for (int c = 0; c < n; c += 64) {
-            const bool a = c + lane < n && tab[c + lane].y > lvl * kBlockM;
+            const bool a = c + lane < n && tab[c + lane].y > lvl * BM;
             total += __builtin_popcountll(__builtin_amdgcn_ballot_w64(a));
         }
         return total;
@@ -275,7 +295,7 @@ struct Kernel {
                                                         int k) {
         const int lane = threadIdx.x & 63;
         for (int c = 0; c < n; c += 64) {
-            const bool a = c + lane < n && tab[c + lane].y > lvl * kBlockM;
+            const bool a = c + lane < n && tab[c + lane].y > lvl * BM;
             const uint64_t m = __builtin_amdgcn_ballot_w64(a);
             const int cnt = __builtin_popcountll(m);
             if (k < cnt) {
@@ -309,7 +329,7 @@ struct Kernel {
         const int S = __builtin_amdgcn_readfirstlane(tab[b].y);
         const int h = p.xcd_lists ? i * 8 + x : i;
         it.bh = b * p.H + h;
-        it.q0 = wk.lvl * kBlockM;
+        it.q0 = wk.lvl * BM;
         it.S = S;
         it.base = ((int64_t)start * p.H + h) * D;
         finish_item(p, it, S);
@@ -318,7 +338,7 @@ struct Kernel {
 
     // Fill in the key-tile range of an item whose bh, q0 (< S) are set.
     static __device__ __forceinline__ void finish_item(const FwdParams &p, Item &it, int S) {
-        const int qlast = min(it.q0 + kBlockM - 1, S - 1);
+        const int qlast = min(it.q0 + BM - 1, S - 1);
         // Keys visible from any row of the item, in whole tiles; tiles outside
         // are never loaded. Every wave walks all of them: a tile hidden from a
         // wave's rows is simply fully masked for that wave.
@@ -363,11 +383,12 @@ struct Kernel {
     // and l when some row's maximum outgrows the slack (always on the first
     // visible tile, where m_run is -inf), and the probabilities: rounded once
     // to the MFMA operand type into pk, summed unrounded into l.
-    // dma(b), b = 0 .. 3, issues one DMA block of the caller's; the four calls
-    // are spread over the exponentials (all of them, in order, on every path).
-    template <typename Dma>
+    // dma(b), b = 0 .. NDMA - 1, issues one DMA block of the caller's; the
+    // calls are spread over the exponentials (all of them, in order, on every
+    // path).
+    template <int NDMA = 4, typename Dma>
     static __device__ __forceinline__ void softmax(State &st, f32x16 (&sacc)[NKB],
-                                                   uint32_t (&pk)[NKB][8], bool masked, int k0,
+                                                   PBuf &pk, bool masked, int k0,
                                                    int qi, int S, int win_lo, int win_hi,
                                                    float c2, int g, const Dma &dma) {
         // Accumulator element r of block kb holds key k0 + 4g + off for query qi,
@@ -388,9 +409,9 @@ struct Kernel {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) pk[kb][r] = 0u;
+                    for (int r = 0; r < NPW; ++r) pk[kb][r] = 0u;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) dma(b);
+                for (int b = 0; b < NDMA; ++b) dma(b);
                 return;
             }
             if (!__builtin_amdgcn_ballot_w64(lo > 0)) {
@@ -440,25 +461,52 @@ struct Kernel {
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, -mu));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, -mu));
-                pk[kb][r >> 1] = Elem<T>::pack(p0, p1);
+                const uint32_t hi = Elem<T>::pack(p0, p1);
+                pk[kb][r >> 1] = hi;
+                if constexpr (kSplitP) {
+                    const float h0 = __builtin_bit_cast(float, hi << 16);
+                    const float h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
+                    pk[kb][8 + (r >> 1)] = Elem<T>::pack(p0 - h0, p1 - h1);
+                }
                 psum0 += p0;
                 psum1 += p1;
                 constexpr int kIters = NKB * 8;  // exponential pairs per lane
+                constexpr int kEvery = kIters / NDMA;
+                static_assert(kEvery * NDMA == kIters, "DMA calls spread evenly");
                 const int it = kb * 8 + (r >> 1);
-                if (it % (kIters / 4) == kIters / 4 - 1) dma(it / (kIters / 4));
+                if (it % kEvery == kEvery - 1) dma(it / kEvery);
             }
         st.l_run += psum0 + psum1;
     }
 
-    // LDS: two K slots then two V slots; relative tile i uses slot i & 1.
-    static __device__ __forceinline__ uint32_t kslot(int i) { return (i & 1) * G::TILE_BYTES; }
-    // After the four tile slots: Q of the workgroup's next item, kBlockM rows in
-    // the K swizzle; wave w's rows 32w .. 32w + 31 are written (DMA) and read
-    // by wave w only.
-    static constexpr uint32_t kQRegion = 4 * G::TILE_BYTES;
+    // LDS: the K slots then the V slots. Without the key split: two of each,
+    // relative tile i in slot i & 1. With it: four of each, group g's tile of
+    // step i in slot 2 (i & 1) + g.
+    static constexpr int NSLOT = KS ? 4 : 2;
+    static __device__ __forceinline__ uint32_t kslot(int i, int grp = 0) {
+        return (KS ? 2 * (i & 1) + grp : (i & 1)) * G::TILE_BYTES;
+    }
+    static __device__ __forceinline__ uint32_t vslot(int i, int grp = 0) {
+        return (NSLOT + (KS ? 2 * (i & 1) + grp : (i & 1))) * G::TILE_BYTES;
+    }
+    // After the tile slots: Q of the workgroup's next item, BM rows in the K
+    // swizzle, 32-row block b read by the wave(s) owning those rows: wave b
+    // (b = w & 3 for both w and w + 4 under the key split, each of which
+    // DMAs half of the block's 1 KiB pieces).
+    static constexpr uint32_t kQRegion = 2 * NSLOT * G::TILE_BYTES;
     // LDS byte offset of the packed-sequence table (after the Q region).
-    static constexpr uint32_t kTabOffset = kQRegion + kBlockM * G::RB;
-    static constexpr int kQBlocks = kWaveRows * G::RB / 1024;  // 1 KiB DMA blocks per wave
+    static constexpr uint32_t kTabOffset = kQRegion + BM * G::RB;
+    static constexpr int kQBlocks = kWaveRows * G::RB / 1024;  // 1 KiB DMA blocks per 32 rows
+    static_assert(kTabOffset <= 160 * 1024, "LDS budget");
+    // The 32-row block of the item (and of the Q region) this wave owns.
+    static __device__ __forceinline__ int row_block(int wave) { return KS ? (wave & 3) : wave; }
+    // The wave's share [lo, hi) of its row block's Q pieces.
+    static __device__ __forceinline__ int qpiece_lo(int wave) {
+        return KS ? (wave >> 2) * (kQBlocks / 2) : 0;
+    }
+    static __device__ __forceinline__ int qpiece_hi(int wave) {
+        return KS ? ((wave >> 2) + 1) * (kQBlocks / 2) : kQBlocks;
+    }
 
     // DMA this wave's 32 rows of the item's Q (rows past S read as zero) into
     // its part of the Q region. Lane L of 1 KiB block b lands in physical
@@ -467,15 +515,16 @@ struct Kernel {
     // Blocks [b0, b1) of the wave's kQBlocks.
     static __device__ __forceinline__ void dma_q(const uint16_t *qh, int q0, int S, int rse,
                                                  uint32_t smem_addr, int wave, int lane,
-                                                 int b0 = 0, int b1 = kQBlocks) {
-        const int r0 = q0 + wave * kWaveRows;
+                                                 int b0, int b1) {
+        const int rb = row_block(wave);
+        const int r0 = q0 + rb * kWaveRows;
         // A wave whose rows all lie past S gets an empty resource: every read
         // returns zero and nothing past the tensor is touched.
         const uint32_t nrec = r0 >= S ? 0u
                               : PACKED ? (uint32_t)(S - r0 - 1) * (uint32_t)rse * 2u + G::RB
                                        : (uint32_t)(S - r0) * G::RB;
         const i32x4 rsrc = buffer_rsrc(qh + (int64_t)r0 * rse, nrec);
-        const uint32_t base = smem_addr + kQRegion + (uint32_t)(wave * kWaveRows) * G::RB;
+        const uint32_t base = smem_addr + kQRegion + (uint32_t)(rb * kWaveRows) * G::RB;
         const int pc = lane % G::CPR;
 #pragma unroll
         for (int b = 0; b < kQBlocks; ++b) {
@@ -485,15 +534,15 @@ struct Kernel {
                       (uint32_t)row * (uint32_t)rse * 2u + (uint32_t)(G::kchunk(pc, row) * 16));
         }
     }
-    static __device__ __forceinline__ uint32_t vslot(int i) {
-        return (2 + (i & 1)) * G::TILE_BYTES;
-    }
 
     // The epilogue of an item for one wave: O = O_acc / l (rounded to the
     // element type), LSE = ln 2 * (m + log2 l).
+    // Blocks [DB0, DB1) of the D / 32 output blocks (all of them unless the key
+    // split divides the row between a pair of waves); the LSE with write_lse.
+    template <int DB0 = 0, int DB1 = NDB>
     static __device__ __forceinline__ void store_output(const FwdParams &p, const State &st,
                                                         int64_t head, int bh, int qi, int S,
-                                                        int rse, int g) {
+                                                        int rse, int g, bool write_lse = true) {
         const float l_tot = sum_with_partner(st.l_run);
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         // Elements 4a .. 4a + 3 of block db hold dims 32db + 8a + 4g + 0..3 of
@@ -505,7 +554,7 @@ struct Kernel {
         // lanes instead of 16 (the O stores otherwise stall the epilogue).
         u32x4 ow[NDB][2];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = DB0; db < DB1; ++db)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const f32x16 &a = st.oacc[db];
@@ -522,11 +571,11 @@ struct Kernel {
         if (qi < S) {
             uint16_t *orow = static_cast<uint16_t *>(p.o) + head + (int64_t)qi * rse;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int db = DB0; db < DB1; ++db)
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
                     *reinterpret_cast<u32x4 *>(orow + 32 * db + 16 * c + 8 * g) = ow[db][c];
-            if (p.lse && g == 0) {
+            if (p.lse && g == 0 && write_lse) {
                 const float lse = l_tot > 0.0f
                                       ? 0.69314718055994531f * (st.m_run + __log2f(l_tot))
                                       : -INFINITY;
@@ -561,6 +610,7 @@ struct Kernel {
         const Item &nx;        // the workgroup's next item (nx.nt == 0: none)
         int64_t head;          // element offset of row 0 of the item's head
         int bh;
+        int nsteps;            // steps of the key loop before the final one (T)
 
         __device__ __forceinline__ bool tile_full(int t) const {
             const int k0 = t * BN;
@@ -586,9 +636,10 @@ struct Kernel {
         // before step 0 ends.
         __device__ __forceinline__ void dma_q_next(int i) const {
             constexpr int kPerPhase = 2;
-            const int b0 = kPerPhase * (i - 1);
-            const int b1 = i == ntiles ? kQBlocks : kPerPhase * i;
-            if (nx.nt > 0 && b0 < kQBlocks)
+            const int lo = qpiece_lo(wave), hi = qpiece_hi(wave);
+            const int b0 = lo + kPerPhase * (i - 1);
+            const int b1 = i == nsteps ? hi : min(hi, lo + kPerPhase * i);
+            if (nx.nt > 0 && b0 < hi)
                 dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, nx), nx.q0,
                       seq_len(S_all, nx), rse, smem_addr, wave, lane, b0, b1);
         }
@@ -604,18 +655,44 @@ struct Kernel {
         // wave, the 32 KiB of a phase queue up behind each other and stall the
         // issuing waves.
         template <bool QK, bool PV, bool DMA>
-        __device__ __forceinline__ void mphase(State &st, f32x16 (&sacc)[NKB],
-                                               const uint32_t (&pk)[NKB][8], int i) const {
+        __device__ __forceinline__ void mphase(State &st, f32x16 (&sacc)[NKB], const PBuf &pk,
+                                               int i) const {
+            TileSrc kt{};
+            if constexpr (DMA) kt = ksrc(i);
+            mcore<QK, PV, DMA ? G::DMA_PER_WAVE : 0>(
+                st, sacc, pk, smem + kslot(kbase + i), smem + vslot(kbase + i - 1),
+                [&](int b) { dma_block(kt, ad.kdma[b], wave, b); });
+        }
+        // The MFMA stream of a phase: P V of the tile whose V^T sits at `vs`
+        // (PV), then the scores of the tile whose K sits at `ks` (QK); with
+        // NDMA > 0, dma(b) for b = 0 .. NDMA - 1 is called once every NS / NDMA
+        // MFMAs.
+        template <bool QK, bool PV, int NDMA, typename Dma>
+        __device__ __forceinline__ void mcore(State &st, f32x16 (&sacc)[NKB], const PBuf &pk,
+                                              const LDS char *ks,
+                                              const LDS char *vs, const Dma &dma) const {
             __builtin_amdgcn_s_setprio(1);
-            const LDS char *vs = smem + vslot(kbase + i - 1);
-            const LDS char *ks = smem + kslot(kbase + i);
-            constexpr int NPV = PV ? NPC * NDB : 0;  // MFMA slot s < NPV: P V chunk s / NDB, block s % NDB
+            // MFMA slot s < NPV: P V chunk c, block db; with the split P, chunk
+            // c's slots are its NDB products of the rounded P, then its NDB of
+            // the remainders, which reuse the V^T operands of the first NDB
+            // (each accumulator's two products stay NDB slots apart).
+            constexpr int NPP = kSplitP ? 2 : 1;
+            constexpr int NPV = PV ? NPC * NDB * NPP : 0;
             constexpr int NQK = QK ? NDC * NKB : 0;  // then S^T chunk q / NKB, block q % NKB
             constexpr int NS = NPV + NQK;
+            auto pv_slot = [](int s, int &c, int &db, int &half) {
+                c = s / (NDB * NPP);
+                half = (s / NDB) % NPP;
+                db = s % NDB;
+            };
+            // LDS reads of slot s (the remainder slots read nothing)
+            auto nreads = [&](int s) { return s < NPV ? ((s / NDB) % NPP == 0 ? 2 : 0) : 1; };
             vec8 a[NS];
             auto load = [&](int s) {
                 if (s < NPV) {
-                    const int c = s / NDB, db = s % NDB;
+                    int c, db, half;
+                    pv_slot(s, c, db, half);
+                    if (half) return;
                     const LDS char *base = vs + ad.v[db] + 16 * c * G::RB;
                     const fp16x4_t lo =
                         __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS fp16x4_t *)(base));
@@ -631,10 +708,15 @@ struct Kernel {
             };
             auto mma = [&](int s) {
                 if (s < NPV) {
-                    const int c = s / NDB, db = s % NDB, kb = c >> 1, hh = c & 1;
-                    const u32x4 pw = {pk[kb][4 * hh + 0], pk[kb][4 * hh + 1], pk[kb][4 * hh + 2],
-                                      pk[kb][4 * hh + 3]};
-                    st.oacc[db] = Elem<T>::mma(a[s], __builtin_bit_cast(vec8, pw), st.oacc[db]);
+                    int c, db, half;
+                    pv_slot(s, c, db, half);
+                    // pairs 4 (c & 1) .. + 3 of block c / 2: words 4 (c & 1) + j
+                    // (rounded) or 8 + 4 (c & 1) + j (remainders)
+                    const int kb = c >> 1, w0 = 8 * half + 4 * (c & 1);
+                    const u32x4 pw = {pk[kb][w0 + 0], pk[kb][w0 + 1], pk[kb][w0 + 2],
+                                      pk[kb][w0 + 3]};
+                    st.oacc[db] = Elem<T>::mma(a[half ? s - NDB : s], __builtin_bit_cast(vec8, pw),
+                                               st.oacc[db]);
                 } else {
                     const int q = s - NPV, c = q / NKB, kb = q % NKB;
                     sacc[kb] = Elem<T>::mma(a[s], st.qf[c], c == 0 ? f32x16{} : sacc[kb]);
@@ -642,41 +724,38 @@ struct Kernel {
             };
 #pragma unroll
             for (int s = 0; s < kDist && s < NS; ++s) load(s);
-            constexpr int DPW = G::DMA_PER_WAVE;
-            constexpr int kPer = NS / DPW;  // MFMAs per DMA block
-            TileSrc kt{};
-            if constexpr (DMA) kt = ksrc(i);
+            constexpr int kPer = NS / (NDMA > 0 ? NDMA : 1);  // MFMAs per DMA block
+            static_assert(NDMA == 0 || kPer * NDMA == NS, "DMA blocks spread evenly");
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 if (s + kDist < NS) load(s + kDist);
                 mma(s);
-                if constexpr (DMA)
-                    if (s % kPer == kPer - 1) dma_block(kt, ad.kdma[s / kPer], wave, s / kPer);
+                if constexpr (NDMA > 0)
+                    if (s % kPer == kPer - 1) dma(s / kPer);
             }
             // Issue order: the first kDist reads, then per slot its look-ahead
             // read(s) and its MFMA.
+            auto read_group = [&](int s) {
+                if (nreads(s) == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                else if (nreads(s) == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            };
 #pragma unroll
-            for (int s = 0; s < kDist && s < NS; ++s) {
-                if (s < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
+            for (int s = 0; s < kDist && s < NS; ++s) read_group(s);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                if (s + kDist < NS) {
-                    if (s + kDist < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
+                if (s + kDist < NS) read_group(s + kDist);
                 __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
             }
             if (QK) pin(sacc);
             if (PV) pin(st.oacc);
             __builtin_amdgcn_s_setprio(0);
+            conservative_lds_wait();
         }
         // With DMA (group 1 in step i + 1, i + 1 < T) the wave issues its
         // share of V(i + 1), one block after each quarter of the exponentials.
         template <bool DMA>
-        __device__ __forceinline__ void vphase(State &st, f32x16 (&sacc)[NKB],
-                                               uint32_t (&pk)[NKB][8], int i) const {
+        __device__ __forceinline__ void vphase(State &st, f32x16 (&sacc)[NKB], PBuf &pk,
+                                               int i) const {
             const int t = t_first + i;
             TileSrc vt{};
             if constexpr (DMA) vt = vsrc(i + 1);
@@ -687,6 +766,7 @@ struct Kernel {
             pin(pk);
             pin(st.l_run);
             pin(st.m_run);
+            conservative_lds_wait();
         }
         // The end of a step: this wave's DMA has landed, then a bare barrier
         // (the kernel orders its own LDS traffic: every LDS read of a step has
@@ -694,7 +774,7 @@ struct Kernel {
         // them, so a slot may be refilled after the barrier).
         static __device__ __forceinline__ void end_step() {
             __builtin_amdgcn_s_waitcnt(0);
-            __builtin_amdgcn_s_barrier();
+            fence_barrier();
         }
 
         // Group 0's share of the K DMA of step i without MFMAs.
@@ -711,12 +791,208 @@ struct Kernel {
         // the two groups' phases aligned: 6% faster there, while at D = 128
         // the halves balance without it (1% faster without).
         static __device__ __forceinline__ void mid_step() {
-            if constexpr (D == 64) __builtin_amdgcn_s_barrier();
+            if constexpr (D == 64 || kConservativeSync) {
+                conservative_lds_wait();
+                fence_barrier();
+            }
         }
+        // ---- key split (KS) --------------------------------------------------------
+        // Group g's step i works on the item's relative tile 2i + g (a tile past
+        // the item's range is an empty source: zero-filled, never read from HBM,
+        // and skipped by every wave). The K tiles of step i + 1 (both groups')
+        // stream in from group 0's MFMA phase of step i, the V tiles of step i
+        // from group 1's softmax phase of step i. Slots: group g's tiles of step
+        // i in K / V slot 2 (i & 1) + g, so step i + 1's refills land in the
+        // slots step i - 1 read, as without the split.
+        static constexpr int DPW = G::DMA_PER_WAVE;
+        __device__ __forceinline__ TileSrc ks_ksrc(int i, int grp) const {
+            const int rel = 2 * (i + 1) + grp;
+            if (i + 1 < nsteps)
+                return tile_src(kh, (t_first + rel) * BN, S, rse,
+                                smem_addr + kslot(kbase + i + 1, grp), rel < ntiles);
+            return tile_src(static_cast<const uint16_t *>(p.k) + head_base(S_all, nx),
+                            (nx.t_first + grp) * BN, seq_len(S_all, nx), rse,
+                            smem_addr + kslot(kbase + i + 1, grp), nx.nt > grp);
+        }
+        __device__ __forceinline__ TileSrc ks_vsrc(int i, int grp) const {
+            const int rel = 2 * i + grp;
+            return tile_src(vh, (t_first + rel) * BN, S, rse, smem_addr + vslot(kbase + i, grp),
+                            rel < ntiles);
+        }
+        // Group 0's K DMA of step i (for step i + 1) without MFMAs; group 1's V
+        // DMA of step i without a softmax.
+        __device__ __forceinline__ void ks_dma_k(int i) const {
+            const TileSrc a = ks_ksrc(i, 0), b = ks_ksrc(i, 1);
+#pragma unroll
+            for (int x = 0; x < DPW; ++x) dma_block(a, ad.kdma[x], wave, x);
+#pragma unroll
+            for (int x = 0; x < DPW; ++x) dma_block(b, ad.kdma[x], wave, x);
+        }
+        __device__ __forceinline__ void ks_dma_v(int i) const {
+            const TileSrc a = ks_vsrc(i, 0), b = ks_vsrc(i, 1);
+#pragma unroll
+            for (int x = 0; x < DPW; ++x) dma_block(a, ad.vdma[x], wave, x);
+#pragma unroll
+            for (int x = 0; x < DPW; ++x) dma_block(b, ad.vdma[x], wave, x);
+        }
+        // M phase of group GRP in step i: P V of its tile of step i - 1 (PV),
+        // the scores of its tile of step i (QK); with DMA (group 0) the K tiles
+        // of step i + 1, one block every NS / (2 DPW) MFMAs.
+        template <int GRP, bool QK, bool PV, bool DMA>
+        __device__ __forceinline__ void ks_mphase(State &st, f32x16 (&sacc)[NKB], const PBuf &pk,
+                                                  int i) const {
+            TileSrc a{}, b{};
+            if constexpr (DMA) {
+                a = ks_ksrc(i, 0);
+                b = ks_ksrc(i, 1);
+            }
+            mcore<QK, PV, DMA ? 2 * DPW : 0>(
+                st, sacc, pk, smem + kslot(kbase + i, GRP), smem + vslot(kbase + i - 1, GRP),
+                [&](int x) { dma_block(x < DPW ? a : b, ad.kdma[x % DPW], wave, x % DPW); });
+        }
+        // Softmax of group GRP's tile of step j; with DMA (group 1) the V tiles
+        // of step j + 1 spread over the exponentials.
+        template <int GRP, bool DMA>
+        __device__ __forceinline__ void ks_vphase(State &st, f32x16 (&sacc)[NKB], PBuf &pk,
+                                                  int j) const {
+            const int t = t_first + 2 * j + GRP;
+            TileSrc a{}, b{};
+            if constexpr (DMA) {
+                a = ks_vsrc(j + 1, 0);
+                b = ks_vsrc(j + 1, 1);
+            }
+            const auto dma = [&](int x) {
+                if constexpr (DMA) dma_block(x < DPW ? a : b, ad.vdma[x % DPW], wave, x % DPW);
+            };
+            softmax<DMA ? 2 * DPW : 4>(st, sacc, pk, !tile_full(t), t * BN, qi, S, win_lo,
+                                       win_hi, c2, g, dma);
+            pin(pk);
+            pin(st.l_run);
+            pin(st.m_run);
+            conservative_lds_wait();
+        }
+        // The key loop of a wave under the key split: steps 0 .. T (T = nsteps),
+        // one barrier each (two at D = 64), like go(). Group 0 runs M_i, V_i,
+        // group 1 V_(i-1), M_i; group 0's steps whose tiles hide every key from
+        // the wave's rows keep only their DMA.
+        template <int GRP>
+        __device__ __forceinline__ void go_ks(State &st) const {
+            f32x16 sacc[NKB];
+            PBuf pk;
+            const int NT = nsteps;
+            // This group's steps whose tile shows the wave's rows a key: [f, l].
+            const int ng = (ntiles - GRP + 1) >> 1;  // this group's tiles
+            int f = 0, l = -1;
+            if (r0 < S) {
+                const int relo = max(0, r0 - win_lo) / BN - t_first;
+                const int rehi = min(S - 1, rlast + win_hi) / BN - t_first;
+                f = max(0, (relo - GRP + 1) >> 1);
+                l = min(ng - 1, (rehi - GRP) >> 1);  // (an arithmetic shift keeps -1)
+            }
+            const bool any = f <= l;
+            if (GRP == 0) {
+                int i = 0;
+                const int fs = any ? f : NT;
+                for (; i < fs; ++i) {
+                    if (i) dma_q_next(i);
+                    ks_dma_k(i);
+                    mid_step();
+                    end_step();
+                }
+                if (any) {
+                    if (i) dma_q_next(i);
+                    ks_mphase<0, true, false, true>(st, sacc, pk, i);
+                    mid_step();
+                    ks_vphase<0, false>(st, sacc, pk, i);
+                    end_step();
+                    for (++i; i <= l; ++i) {
+                        dma_q_next(i);
+                        ks_mphase<0, true, true, true>(st, sacc, pk, i);
+                        mid_step();
+                        ks_vphase<0, false>(st, sacc, pk, i);
+                        end_step();
+                    }
+                    dma_q_next(i);
+                    if (i < NT) ks_mphase<0, false, true, true>(st, sacc, pk, i);
+                    else ks_mphase<0, false, true, false>(st, sacc, pk, i);
+                    mid_step();
+                    end_step();
+                    ++i;
+                }
+                for (; i <= NT; ++i) {
+                    if (i) dma_q_next(i);
+                    if (i < NT) ks_dma_k(i);
+                    mid_step();
+                    end_step();
+                }
+            } else {
+                // Group 1 walks all of its steps: a tile hidden from the wave's
+                // rows (at most one at either end of an item) takes the masked
+                // softmax's all-hidden path, P = 0. (Skipping those steps, as
+                // group 0 does, made the compiler spill registers here.)
+                ks_dma_v(0);
+                mid_step();
+                ks_mphase<1, true, false, false>(st, sacc, pk, 0);
+                end_step();
+                for (int i = 1; i < NT; ++i) {
+                    dma_q_next(i);
+                    ks_vphase<1, true>(st, sacc, pk, i - 1);
+                    mid_step();
+                    ks_mphase<1, true, true, false>(st, sacc, pk, i);
+                    end_step();
+                }
+                dma_q_next(NT);
+                ks_vphase<1, false>(st, sacc, pk, NT - 1);
+                mid_step();
+                ks_mphase<1, false, true, false>(st, sacc, pk, NT);
+                end_step();
+            }
+        }
+        // End of an item under the key split: waves w and w ^ 4 hold the same
+        // rows' (O, m, l) over complementary key tiles. Each keeps half of the
+        // output blocks (group 0 the first half) and hands the other half, with
+        // its m and l, to its partner through LDS: the V slots (free once the
+        // last step's P V has read them) take the O halves, the K slots of the
+        // last step's parity (the next item's first K tiles went to the other
+        // parity) take m and l. Merged: m = max(m_a, m_b), O = 2^(m_a - m) O_a +
+        // 2^(m_b - m) O_b, likewise l. The second barrier keeps the next item's
+        // DMA into these slots behind every read.
+        template <int GRP>
+        __device__ __forceinline__ void ks_merge(State &st) const {
+            constexpr int NH = NDB / 2;
+            constexpr int GIVE = GRP == 0 ? NH : 0, KEEP = GRP == 0 ? 0 : NH;
+            LDS float *xo = (LDS float *)(smem + vslot(0, 0));
+            LDS float *xm = (LDS float *)(smem + kslot(kbase + nsteps - 1, 0));
+#pragma unroll
+            for (int k = 0; k < NH; ++k)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    xo[((wave * NH + k) * 16 + e) * 64 + lane] = st.oacc[GIVE + k][e];
+            xm[wave * 128 + lane] = st.m_run;
+            xm[wave * 128 + 64 + lane] = st.l_run;
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            fence_barrier();
+            const int pw = wave ^ 4;
+            const float mp = xm[pw * 128 + lane], lp = xm[pw * 128 + 64 + lane];
+            const float m = fmaxf(st.m_run, mp);
+            const float as = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.m_run - m);
+            const float ap = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mp - m);
+#pragma unroll
+            for (int k = 0; k < NH; ++k)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    st.oacc[KEEP + k][e] =
+                        as * st.oacc[KEEP + k][e] + ap * xo[((pw * NH + k) * 16 + e) * 64 + lane];
+            st.l_run = as * st.l_run + ap * lp;
+            st.m_run = m;
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            fence_barrier();
+        }
+
         template <int GRP>
         __device__ __forceinline__ bool go(State &st) const {
             f32x16 sacc[NKB];
-            uint32_t pk[NKB][8];
+            PBuf pk;
             const int nt = ntiles;  // >= 1
             // The last tile (relative) with a key visible to this wave's rows:
             // past it, M_i and V_i have nothing to do for the wave.
@@ -822,12 +1098,15 @@ struct Kernel {
         Item it = next_item(p, tab, wk, r);
         if (PACKED && it.nt == 0) return;  // every sequence is shorter than the workgroup's share
         {
-            if (grp == 0)
+            // K of the first step: tile 0 (and, under the key split, tile 1 from group 1)
+            if (grp == 0 || KS)
                 load_tile(tile_src(static_cast<const uint16_t *>(p.k) + head_base(S_all, it),
-                                   it.t_first * BN, seq_len(S_all, it), rse, smem_addr + kslot(0)),
+                                   (it.t_first + grp) * BN, seq_len(S_all, it), rse,
+                                   smem_addr + kslot(0, grp), it.nt > grp),
                           ad.kdma, wave);
             dma_q(static_cast<const uint16_t *>(p.q) + head_base(S_all, it), it.q0,
-                  seq_len(S_all, it), rse, smem_addr, wave, lane);
+                  seq_len(S_all, it), rse, smem_addr, wave, lane, qpiece_lo(wave),
+                  qpiece_hi(wave));
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -841,7 +1120,7 @@ struct Kernel {
             const uint16_t *vh = static_cast<const uint16_t *>(p.v) + head;
 
             // This wave's rows.
-            const int r0 = it.q0 + wave * kWaveRows;
+            const int r0 = it.q0 + row_block(wave) * kWaveRows;
             const int rlast = min(r0 + kWaveRows - 1, S - 1);
             const int qi = r0 + l32;  // this lane's query row
 
@@ -849,7 +1128,7 @@ struct Kernel {
             // is row l32, logical chunk 2c + g, the K read pattern.
             State st;
             {
-                const LDS char *qs = smem + kQRegion + wave * kWaveRows * G::RB;
+                const LDS char *qs = smem + kQRegion + row_block(wave) * kWaveRows * G::RB;
                 const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
 #pragma unroll
                 for (int c = 0; c < NDC; ++c) {
@@ -868,21 +1147,33 @@ struct Kernel {
             st.m_run = -INFINITY;
             st.l_run = 0.0f;
 
+            const int nsteps = KS ? (it.nt + 1) >> 1 : it.nt;
             Loop loop{p,     smem,   smem_addr, kh, vh,   S,  S_all,  rse, it.t_first, it.nt,
                       it.t_in_lo, it.t_in_hi, r0, rlast, qi, win_lo, win_hi, c2,  g, wave,
-                      lane,  ad,     kbase,     nx,   head, it.bh};
-            const bool stored = grp == 0 ? loop.template go<0>(st) : loop.template go<1>(st);
-
-            if (!stored) store_output(p, st, head, it.bh, qi, S, rse, g);
-            kbase += it.nt;
+                      lane,  ad,     kbase,     nx,   head, it.bh, nsteps};
+            if constexpr (KS) {
+                if (grp == 0) {
+                    loop.template go_ks<0>(st);
+                    loop.template ks_merge<0>(st);
+                    store_output<0, NDB / 2>(p, st, head, it.bh, qi, S, rse, g, true);
+                } else {
+                    loop.template go_ks<1>(st);
+                    loop.template ks_merge<1>(st);
+                    store_output<NDB / 2, NDB>(p, st, head, it.bh, qi, S, rse, g, false);
+                }
+            } else {
+                const bool stored = grp == 0 ? loop.template go<0>(st) : loop.template go<1>(st);
+                if (!stored) store_output(p, st, head, it.bh, qi, S, rse, g);
+            }
+            kbase += nsteps;
             it = nx;
         }
     }
 };
 
-template <typename T, int D, bool PACKED, bool ROPE>
+template <typename T, int D, bool PACKED, bool ROPE, bool KS>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(FwdParams p) {
-    typedef Kernel<T, D, PACKED, ROPE> K;
+    typedef Kernel<T, D, PACKED, ROPE, KS> K;
     __shared__ __attribute__((aligned(1024)))
     char smem[K::kTabOffset + (PACKED ? kMaxPackedSeqs * 8 : 0)];
     K::run(p, (LDS char *)smem);
@@ -893,9 +1184,12 @@ hipError_t launch_t(const FwdParams &p, hipStream_t stream) {
     void *args[] = {const_cast<FwdParams *>(&p)};
     // packed sequences take no rotary embedding
     const void *fn =
-        p.cu_seqlens ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, true, false>)
-        : p.rope_cos ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, true>)
-                     : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, false>);
+        p.cu_seqlens  ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, true, false, false>)
+        : p.rope_cos  ? (p.key_split
+                             ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, true, true>)
+                             : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, true, false>))
+        : p.key_split ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, false, true>)
+                      : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, false, false>);
     return hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, 0, stream);
 }
 
