@@ -23,8 +23,9 @@
  *     ops-transformer walkthrough, pitfall 3, and the tile-fusion page,
  *     section 10 (best practice).
  *
- * All functions are reentrant and thread-safe; the library keeps no state and
- * allocates no memory (fa_decode's workspace is the caller's).
+ * All functions are reentrant and thread-safe and allocate no memory
+ * (fa_decode's workspace is the caller's). The only state is the per-device
+ * address of the scratch array fa_decode_noalloc uses, looked up once.
  */
 #ifndef FA_H
 #define FA_H
@@ -305,6 +306,29 @@ int fa_decode(const void *q, const void *k, const void *v, void *o, float *lse,
  */
 int64_t fa_decode_workspace_bytes(int B, int H, int Sq, int Sk, int D, int mask_mode, int win_l,
                                   int win_r);
+
+/*
+ * fa_decode_noalloc -- fa_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The split partials go to a scratch
+ * array the library holds in device memory, one copy per GPU, alive until the
+ * process ends; the call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). The first call on a device looks up that
+ * device's copy (hipGetSymbolAddress); later calls reuse the address.
+ *
+ * Arguments, layout, ownership, results and error rules: as fa_decode with
+ * the workspace taken from the scratch array. Additionally FA_ERR_TOO_LARGE
+ * when the split partials would exceed the scratch array's 24 MiB
+ * (fa_decode_workspace_bytes(...) > 25165824; no shape does on a 256-CU
+ * device), and FA_ERR_HIP when the array's address cannot be looked up.
+ * Nothing in the array needs to start at zero: every partial the merge
+ * reads is written by the same call. Calls on one GPU share its array, so
+ * calls that may overlap in time on one GPU (other streams, other threads)
+ * race and give undefined results; calls on one stream are ordered and safe.
+ */
+int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int B, int H, int Sq, int Sk, int D, float scale, int mask_mode,
+                      int win_l, int win_r, int dtype, hipStream_t stream);
 
 /*
  * fa_decode_paged -- fa_decode over a paged key/value cache (serving layout).

@@ -6,10 +6,10 @@ A thin ctypes binding over ``libfa.so`` (the C ABI in ``include/fa.h``).
 ``fa_bwd_workspace_bytes``, ``fa_bwd_flops``, ``fa_decode``, ``fa_decode_rope``,
 ``fa_decode_paged_rope``,
 ``fa_decode_workspace_bytes``, ``fa_decode_flops``, ``fa_decode_paged``,
-``fa_decode_paged_workspace_bytes`` and ``fa_strerror``
+``fa_decode_paged_workspace_bytes``, ``fa_decode_noalloc`` and ``fa_strerror``
 carry the C names and arguments (marshalling only). ``forward``,
-``forward_varlen``, ``rope``, ``forward_rope``, ``backward``, ``decode``
-and ``decode_paged`` are the convenience entries
+``forward_varlen``, ``rope``, ``forward_rope``, ``backward``, ``decode``,
+``decode_noalloc`` and ``decode_paged`` are the convenience entries
 for torch tensors: torch supplies device memory and the stream; every step of
 the computation runs in the library's HIP kernels.
 There is no fallback: if the library is missing, importing this package
@@ -25,8 +25,8 @@ __all__ = [
     "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_rope", "fa_fwd_rope", "FA_ROPE_HALVES",
     "FA_ROPE_INTERLEAVED", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_flops", "fa_decode",
     "fa_decode_rope", "fa_decode_paged_rope", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
-    "fa_decode_paged_workspace_bytes", "fa_strerror", "forward",
-    "forward_varlen", "rope", "forward_rope", "backward", "decode",
+    "fa_decode_paged_workspace_bytes", "fa_decode_noalloc", "fa_strerror", "forward",
+    "forward_varlen", "rope", "forward_rope", "backward", "decode", "decode_noalloc",
     "decode_paged", "lib_path", "library", "load_library",
 ]
 
@@ -93,6 +93,9 @@ def _load(path=None):
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci,
                               ci, ci, vp, i64, vp]
     lib.fa_decode.restype = ci
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float,
+                                      ci, ci, ci, ci, vp]
+    lib.fa_decode_noalloc.restype = ci
     lib.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci]
     lib.fa_decode_workspace_bytes.restype = i64
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
@@ -192,6 +195,13 @@ def fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, 
     """Call ``fa_decode`` with raw device addresses (ints); return its status."""
     return _lib.fa_decode(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r,
                           dtype, workspace, workspace_bytes, stream)
+
+
+def fa_decode_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
+                      stream):
+    """Call ``fa_decode_noalloc`` with raw device addresses (ints); return its status."""
+    return _lib.fa_decode_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l,
+                                  win_r, dtype, stream)
 
 
 def fa_decode_rope(q, k, v, o, lse, cos_table, sin_table, n_pos, rope_mode, B, H, Sq, Sk, D,
@@ -561,6 +571,52 @@ def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse
                                     int(ws_bytes), stream)
     if status != 0:
         raise FaError(status, "fa_decode" if rope is None else "fa_decode_rope")
+    return out, lse
+
+
+def decode_noalloc(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse=None,
+                   return_lse=True, stream=None):
+    """``decode`` through ``fa_decode_noalloc``: the split partials go to the
+    library's per-GPU scratch array instead of a workspace, so with ``out``
+    (and ``lse``, or ``return_lse=False``) given nothing is allocated. Calls
+    that overlap in time on one GPU race on that array. Returns ``(o, lse)``."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, Sq, D] and k, v one [B, H, Sk, D] shape")
+    B, H, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D:
+        raise ValueError("q and k, v disagree on B, H or D")
+    Sk = k.shape[2]
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must all be float16 or all bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Sq) or lse.dtype != torch.float32
+                            or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor on q's device")
+    wl, wr = window
+    m = _mask_code(mask)
+    dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    with torch.cuda.device(q.device):
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        status = fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, B, H, Sq, Sk, D,
+                                   float(scale), m, int(wl), int(wr), dtype, stream)
+    if status != 0:
+        raise FaError(status, "fa_decode_noalloc")
     return out, lse
 
 

@@ -700,6 +700,21 @@ extern "C" int fa_decode(const void *q, const void *k, const void *v, void *o, f
                          workspace, workspace_bytes, stream, nullptr, nullptr, 0, 0, 0);
 }
 
+extern "C" int fa_decode_noalloc(const void *q, const void *k, const void *v, void *o,
+                                 float *lse, int B, int H, int Sq, int Sk, int D, float scale,
+                                 int mask_mode, int win_l, int win_r, int dtype,
+                                 hipStream_t stream) {
+    DecodePlan pl;
+    const int rc = plan_decode(B, H, Sq, Sk, D, mask_mode, win_l, win_r, false, &pl);
+    if (rc != FA_OK) return rc;
+    if (pl.empty) return FA_OK;
+    if (pl.ws_bytes > fa::kDecodeScratchBytes) return FA_ERR_TOO_LARGE;
+    void *ws = nullptr;
+    if (pl.ws_bytes > 0 && fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+    return decode_common(q, k, v, o, lse, B, H, Sq, Sk, D, scale, mask_mode, win_l, win_r, dtype,
+                         ws, pl.ws_bytes, stream, nullptr, nullptr, 0, 0, 0);
+}
+
 extern "C" int fa_decode_paged(const void *q, const void *k_pages, const void *v_pages, void *o,
                                float *lse, const int32_t *block_table, const int32_t *seq_lens,
                                int B, int H, int Sq, int max_seq_len, int D, int num_pages,

@@ -40,10 +40,37 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// Split partials of fa_decode_noalloc: one copy of this array per GPU. Host
+// code never passes its name to a kernel (on the host it names a stand-in, not
+// device memory); it uses the address decode_scratch() looks up.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *a = nullptr;
+        err = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));  // with `dev` current
+        if (err != hipSuccess) return err;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 namespace {
 

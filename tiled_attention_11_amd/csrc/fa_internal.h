@@ -132,4 +132,15 @@ struct DecodeParams {
 // Enqueue the cache kernel (and, for nsplit > 1, the merge kernel).
 hipError_t launch_decode(const DecodeParams &p, int D, int dtype, hipStream_t stream);
 
+// Bytes of the device-resident scratch array that the allocation-free cache
+// entry point uses for its split partials (one copy per GPU, alive until the
+// process ends). A plan on a 256-CU device needs at most about 17 MB
+// (B*H*nsplit < 2 * 512 splits of 32 rows of D + 1 floats).
+constexpr int64_t kDecodeScratchBytes = 24ll << 20;
+
+// Device address of the current device's scratch array, looked up
+// (hipGetSymbolAddress) on the first call made with that device current and
+// cached per device afterwards. No allocation.
+hipError_t decode_scratch(void **ptr);
+
 }  // namespace fa
