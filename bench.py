@@ -686,8 +686,9 @@ def main():
         "median_launch_us": round(float(np.median(per)) * 1e6, 2),
         "min_launch_us": round(float(np.min(per)) * 1e6, 2),
         "tflops_at_median": round(flops / float(np.median(per)) / 1e12, 2),
-        # the shader clock under this load (sysfs DPM level, sampled during the
-        # timed launches) and the dense fp16 MFMA peak at that clock
+        # the shader clock under this load (sysfs DPM level, sampled over the
+        # same launches run again right after the timed region) and the dense
+        # fp16 MFMA peak at that clock
         "sclk_mhz": clk.mhz(),
         "pct_of_clock_adjusted_peak": (round(100.0 * tflops / (256 * 4096 * clk.mhz() * 1e-6), 2)
                                        if clk.mhz() else None),
