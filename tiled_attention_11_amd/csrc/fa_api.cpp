@@ -108,14 +108,41 @@ int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int
     if (xcd) grid -= grid % kNumXcd;
     const uint64_t list_heads = xcd ? bh / kNumXcd : bh;
     const uint64_t nj = xcd ? grid / kNumXcd : grid;  // workgroups per list
-    // Heads per group: enough that a round of nj positions covers about one
-    // group, so the workgroups of a list share few heads at a time.
+    // The flat part (dense layout only): the last query tiles of a head that
+    // walk the most key tiles, all alike (a sliding window's tiles past the
+    // window's length). Taken first when it is at least two tiles (a causal
+    // mask has one costliest tile per head: the grouped order pairs its tiles
+    // best), fills at least one round of the list and is not the whole head
+    // (a full mask keeps the grouped order).
+    uint64_t n_flat = 0;
+    if (!p.cu_seqlens) {
+        const int bn = fa::fwd_key_tile(D);
+        auto tiles = [&](uint64_t qt) {
+            const int64_t q0 = (int64_t)qt * block_m;
+            const int64_t qlast = std::min<int64_t>(q0 + block_m - 1, (int64_t)rows - 1);
+            const int64_t first = std::max<int64_t>(0, q0 - p.win_lo) / bn;
+            const int64_t last = std::min<int64_t>((int64_t)rows - 1, qlast + p.win_hi) / bn;
+            return last - first + 1;
+        };
+        int64_t most = 0;
+        for (uint64_t qt = 0; qt < n_qtiles; ++qt) most = std::max(most, tiles(qt));
+        while (n_flat < n_qtiles && tiles(n_qtiles - 1 - n_flat) == most) ++n_flat;
+        bool suffix = true;  // every tile below the flat part costs less
+        for (uint64_t qt = 0; qt + n_flat < n_qtiles && suffix; ++qt) suffix = tiles(qt) < most;
+        if (!suffix || n_flat < 2 || n_flat == n_qtiles || list_heads * n_flat < nj) n_flat = 0;
+    }
+    // Heads per group (of the tiles below the flat part): enough that a round
+    // of nj positions covers about one group, so the workgroups of a list
+    // share few heads at a time.
+    const uint64_t n_rest = n_qtiles - n_flat;
     uint64_t gh = 1;
-    while (2 * gh * n_qtiles <= nj && list_heads % (2 * gh) == 0) gh *= 2;
+    while (2 * gh * n_rest <= nj && list_heads % (2 * gh) == 0) gh *= 2;
     p.grid = (int)grid;
     p.xcd_lists = xcd;
     p.list_len = (int)(list_heads * n_qtiles);
     p.group_heads = (int)gh;
+    p.n_flat = (int)n_flat;
+    p.flat_items = (int)(list_heads * n_flat);
     hipError_t err = fa::launch_fwd(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

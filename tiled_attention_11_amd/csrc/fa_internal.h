@@ -29,11 +29,16 @@ struct FwdParams {
     // workgroups w = x mod 8; otherwise one list holds every head. list_len:
     // items per list; group_heads: heads per group within a list (divides the
     // list's heads). Packed sequences order their lists by query tile instead
-    // and use neither.
+    // and use neither. n_flat > 0: the last n_flat query tiles of every head
+    // cost the same (the most) and take the first flat_items = heads in the
+    // list * n_flat positions of a list, head after head; the remaining tiles
+    // (the cheaper ones) follow in groups of group_heads as above.
     int grid;
     int xcd_lists;
     int list_len;
     int group_heads;
+    int n_flat;
+    int flat_items;
     // Row addressing. Row r of head h of sequence b starts at element
     // base + r * row_stride; its LSE at index lse_base + r * lse_stride.
     //   [B, H, S, D]:      base = (b*H + h)*S*D, row_stride = D;
@@ -72,6 +77,8 @@ hipError_t launch_rope(const RopeParams &p, int D, int dtype, hipStream_t stream
 // Query rows per work item of the forward kernel, and of its key-split variant.
 constexpr int kBlockM = 256;
 constexpr int kBlockMSplit = 128;
+// Keys per tile of the forward kernel (16 KiB of K or V either way).
+constexpr int fwd_key_tile(int D) { return D == 128 ? 64 : 128; }
 // Sequences of one packed launch (the kernel keeps a table of them in LDS);
 // the host splits larger batches over several launches.
 constexpr int kMaxPackedSeqs = 1024;

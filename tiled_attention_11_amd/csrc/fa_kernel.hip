@@ -68,7 +68,7 @@ static_assert(kWaves * kWaveRows == kBlockM, "workgroup covers kBlockM rows");
 // D = 128: 64-key tiles; D = 64: 128-key tiles. Either way a K or V tile is
 // 16 KiB, a wave issues 32 MFMAs per tile, and a stage (K + V) is 32 KiB.
 template <int D> struct Geom {
-    static constexpr int BN = (D == 128) ? 64 : 128;   // keys per tile
+    static constexpr int BN = fwd_key_tile(D);   // keys per tile
     static constexpr int RB = 2 * D;                   // bytes per K/V row
     static constexpr int CPR = RB / 16;                // 16-byte chunks per row
     static constexpr int TILE_BYTES = BN * RB;         // one K or V tile
@@ -248,21 +248,34 @@ struct Kernel {
         return r * nj + ((r & 1) ? nj - 1 - j : j);
     }
 
-    // [B, H, S, D]: list position -> item. A list runs its heads in groups of
-    // group_heads, and each group's query tiles from the last to the first,
-    // the group's heads interleaved.
+    // [B, H, S, D]: list position -> item. Under a sliding window most query
+    // tiles of a head walk the same number of key tiles (the flat part, the
+    // last n_flat tiles): those come first, head after head, each head's from
+    // the last tile down, and the snake deals them out evenly whatever their
+    // order. Then (or from the start, n_flat = 0) a list runs its heads in
+    // groups of group_heads, each group's remaining query tiles from the last
+    // to the first, the group's heads interleaved: a round of the snake then
+    // pairs a group's costliest tile with its cheapest.
     static __device__ __forceinline__ Item item_of(const FwdParams &p, int r) {
         Item it;
-        const int nq = p.n_qtiles;
         int x;
         const int pos = list_pos(p, r, x);
         it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = 0;
         if (pos >= p.list_len) return it;
-        const int gh = p.group_heads;
-        const int per_group = gh * nq;
-        const int grp = pos / per_group, within = pos - grp * per_group;
-        const int qt = nq - 1 - within / gh;
-        const int hl = grp * gh + within % gh;
+        int qt, hl;
+        if (pos < p.flat_items) {
+            const int nf = p.n_flat;
+            hl = pos / nf;
+            qt = p.n_qtiles - 1 - (pos - hl * nf);
+        } else {
+            const int rp = pos - p.flat_items;
+            const int nq = p.n_qtiles - p.n_flat;  // tiles below the flat part
+            const int gh = p.group_heads;
+            const int per_group = gh * nq;
+            const int grp = rp / per_group, within = rp - grp * per_group;
+            qt = nq - 1 - within / gh;
+            hl = grp * gh + within % gh;
+        }
         it.bh = p.xcd_lists ? hl * 8 + x : hl;
         it.q0 = qt * BM;
         finish_item(p, it, p.S);
