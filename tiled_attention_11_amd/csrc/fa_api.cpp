@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <functional>
 
 namespace {
 
@@ -82,6 +83,57 @@ int device_cus(int *n_cu) {
     return FA_OK;
 }
 
+// Work lists for a persistent grid over bh heads of `levels` items each
+// (fa::ListPlan). xcd_ok: the heads split evenly over the 8 XCD lists. cost
+// (may be empty): an item's relative cost by level, which selects the flat
+// part: the last levels of a head that cost the most, all alike (a sliding
+// window's tiles past the window's length), taken first when there are at
+// least two of them (a causal mask has one costliest tile per head: the
+// grouped order pairs its tiles best), they fill at least one round of the
+// list and they are not the whole head (a full mask keeps the grouped order).
+fa::ListPlan plan_lists(uint64_t bh, uint64_t levels, bool xcd_ok, int n_cu,
+                        const std::function<int64_t(uint64_t)> &cost) {
+    const uint64_t n_items = bh * levels;
+    uint64_t grid = n_items < (uint64_t)n_cu ? n_items : (uint64_t)n_cu;
+    const bool xcd = xcd_ok && grid >= (uint64_t)kNumXcd;
+    if (xcd) grid -= grid % kNumXcd;
+    const uint64_t list_heads = xcd ? bh / kNumXcd : bh;
+    const uint64_t nj = xcd ? grid / kNumXcd : grid;  // workgroups per list
+    uint64_t n_flat = 0;
+    if (cost) {
+        int64_t most = 0;
+        for (uint64_t l = 0; l < levels; ++l) most = std::max(most, cost(l));
+        while (n_flat < levels && cost(levels - 1 - n_flat) == most) ++n_flat;
+        bool suffix = true;  // every level below the flat part costs less
+        for (uint64_t l = 0; l + n_flat < levels && suffix; ++l) suffix = cost(l) < most;
+        if (!suffix || n_flat < 2 || n_flat == levels || list_heads * n_flat < nj) n_flat = 0;
+    }
+    // Heads per group (of the levels below the flat part): enough that a
+    // round of nj positions covers about one group, so the workgroups of a
+    // list share few heads at a time.
+    const uint64_t n_rest = levels - n_flat;
+    uint64_t gh = 1;
+    while (2 * gh * n_rest <= nj && list_heads % (2 * gh) == 0) gh *= 2;
+    fa::ListPlan pl;
+    pl.grid = (int)grid;
+    pl.xcd_lists = xcd;
+    pl.list_len = (int)(list_heads * levels);
+    pl.levels = (int)levels;
+    pl.group_heads = (int)gh;
+    pl.n_flat = (int)n_flat;
+    pl.flat_items = (int)(list_heads * n_flat);
+    return pl;
+}
+
+// Tiles of `tile` keys (or queries) that rows r0 .. r1 see under the window
+// [i - lo, i + hi] (clipped to 0 .. S - 1): the key tiles of a query tile,
+// or, with lo and hi swapped, the query tiles of a key tile.
+int64_t tiles_seen(int64_t r0, int64_t r1, int64_t S, int64_t lo, int64_t hi, int64_t tile) {
+    const int64_t first = std::max<int64_t>(0, r0 - lo) / tile;
+    const int64_t last = std::min<int64_t>(S - 1, r1 + hi) / tile;
+    return last - first + 1;
+}
+
 // rows: the sequence length that sets the item count (the longest sequence
 // when packed). allow_split: the layout may use the key-split variant.
 int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int dtype,
@@ -100,49 +152,19 @@ int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int
     const uint64_t n_qtiles = (rows + block_m - 1) / block_m;
     p.key_split = split;
     p.n_qtiles = (int)n_qtiles;
-    const uint64_t n_items = bh * n_qtiles;
-    uint64_t grid = n_items < (uint64_t)n_cu ? n_items : (uint64_t)n_cu;
-    // Packed sequences split heads over the lists by h % 8 within every sequence.
-    const bool xcd = (p.cu_seqlens ? p.H % kNumXcd == 0 : bh % kNumXcd == 0) &&
-                     grid >= (uint64_t)kNumXcd;
-    if (xcd) grid -= grid % kNumXcd;
-    const uint64_t list_heads = xcd ? bh / kNumXcd : bh;
-    const uint64_t nj = xcd ? grid / kNumXcd : grid;  // workgroups per list
-    // The flat part (dense layout only): the last query tiles of a head that
-    // walk the most key tiles, all alike (a sliding window's tiles past the
-    // window's length). Taken first when it is at least two tiles (a causal
-    // mask has one costliest tile per head: the grouped order pairs its tiles
-    // best), fills at least one round of the list and is not the whole head
-    // (a full mask keeps the grouped order).
-    uint64_t n_flat = 0;
+    // Packed sequences split heads over the lists by h % 8 within every
+    // sequence, and order items by their own walk (no costs here).
+    const bool xcd_ok = p.cu_seqlens ? p.H % kNumXcd == 0 : bh % kNumXcd == 0;
+    std::function<int64_t(uint64_t)> cost;
     if (!p.cu_seqlens) {
-        const int bn = fa::fwd_key_tile(D);
-        auto tiles = [&](uint64_t qt) {
+        const int64_t bn = fa::fwd_key_tile(D), S = (int64_t)rows;
+        const int64_t lo = p.win_lo, hi = p.win_hi;
+        cost = [=](uint64_t qt) {
             const int64_t q0 = (int64_t)qt * block_m;
-            const int64_t qlast = std::min<int64_t>(q0 + block_m - 1, (int64_t)rows - 1);
-            const int64_t first = std::max<int64_t>(0, q0 - p.win_lo) / bn;
-            const int64_t last = std::min<int64_t>((int64_t)rows - 1, qlast + p.win_hi) / bn;
-            return last - first + 1;
+            return tiles_seen(q0, std::min<int64_t>(q0 + block_m - 1, S - 1), S, lo, hi, bn);
         };
-        int64_t most = 0;
-        for (uint64_t qt = 0; qt < n_qtiles; ++qt) most = std::max(most, tiles(qt));
-        while (n_flat < n_qtiles && tiles(n_qtiles - 1 - n_flat) == most) ++n_flat;
-        bool suffix = true;  // every tile below the flat part costs less
-        for (uint64_t qt = 0; qt + n_flat < n_qtiles && suffix; ++qt) suffix = tiles(qt) < most;
-        if (!suffix || n_flat < 2 || n_flat == n_qtiles || list_heads * n_flat < nj) n_flat = 0;
     }
-    // Heads per group (of the tiles below the flat part): enough that a round
-    // of nj positions covers about one group, so the workgroups of a list
-    // share few heads at a time.
-    const uint64_t n_rest = n_qtiles - n_flat;
-    uint64_t gh = 1;
-    while (2 * gh * n_rest <= nj && list_heads % (2 * gh) == 0) gh *= 2;
-    p.grid = (int)grid;
-    p.xcd_lists = xcd;
-    p.list_len = (int)(list_heads * n_qtiles);
-    p.group_heads = (int)gh;
-    p.n_flat = (int)n_flat;
-    p.flat_items = (int)(list_heads * n_flat);
+    p.plan = plan_lists(bh, n_qtiles, xcd_ok, n_cu, cost);
     hipError_t err = fa::launch_fwd(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -499,6 +521,22 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
     p.win_lo = win_lo;
     p.win_hi = win_hi;
     p.scale = scale;
+    // Persistent grids over 256-row tiles: dQ items are query tiles (cost:
+    // the 64-key tiles they see), dK/dV items key tiles, the level counting
+    // down from the last tile (cost: the 32-query tiles that see them).
+    int n_cu = 0;
+    if (device_cus(&n_cu) != FA_OK) return FA_ERR_HIP;
+    const int64_t rows = fa::kBwdRows, SS = S, lo = win_lo, hi = win_hi;
+    const uint64_t ntiles = ((uint64_t)S + rows - 1) / rows;
+    const bool xcd_ok = bh % kNumXcd == 0;
+    p.dq_plan = plan_lists(bh, ntiles, xcd_ok, n_cu, [=](uint64_t qt) {
+        const int64_t q0 = (int64_t)qt * rows;
+        return tiles_seen(q0, std::min<int64_t>(q0 + rows - 1, SS - 1), SS, lo, hi, 64);
+    });
+    p.kv_plan = plan_lists(bh, ntiles, xcd_ok, n_cu, [=](uint64_t l) {
+        const int64_t k0 = (int64_t)(ntiles - 1 - l) * rows;
+        return tiles_seen(k0, std::min<int64_t>(k0 + rows - 1, SS - 1), SS, hi, lo, 32);
+    });
     return fa::launch_bwd(p, D, dtype, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -33,7 +33,8 @@
 //  (the A operand of the accumulating product), so it is stored twice, once
 //  per LDS swizzle, which keeps both read patterns free of bank conflicts.
 //  Hidden pairs get the exponent -inf by a select, never a branch. Both
-//  grids run their heaviest row tiles first across all heads. dQ and dK/dV
+//  kernels run persistent workgroups over the forward's work lists (a
+//  head's tiles on one XCD's L2, costly and cheap tiles paired). dQ and dK/dV
 //  each own their outputs, so there are no atomics and the results are
 //  deterministic.
 
@@ -53,6 +54,7 @@ using namespace dev;
 // wave's VALU work run beside the other's MFMAs.
 constexpr int kDqWaves = 8;
 constexpr int kKvWaves = 8;
+static_assert(32 * kDqWaves == kBwdRows && 32 * kKvWaves == kBwdRows, "work item rows");
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D, int BN_> struct BGeom {
@@ -199,21 +201,26 @@ struct Bwd {
     // LDS per stage: K rows (row swizzle), K (transposed swizzle), V rows.
     static constexpr uint32_t kDqStage = 3 * G::TILE_BYTES;
 
+    // The workgroup's items from its work list (persistent grid; see
+    // ListPlan): a head's query tiles on one XCD, few heads per XCD at a
+    // time, costly and cheap tiles paired. An item's LDS stages are free for
+    // the next one after a barrier.
     static __device__ void dq(const BwdParams &p, LDS char *smem) {
+        for (int r = 0;; ++r) {
+            int x, bh, qt;
+            const int pos = list_pos(p.dq_plan, r, x);
+            if (!list_item(p.dq_plan, x, pos, bh, qt)) break;
+            if (r) __syncthreads();
+            dq_item(p, smem, __builtin_amdgcn_readfirstlane(bh), __builtin_amdgcn_readfirstlane(qt));
+        }
+    }
+    static __device__ __forceinline__ void dq_item(const BwdParams &p, LDS char *smem, int bh,
+                                                   int qt) {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int l32 = lane & 31, g = lane >> 5;
         const int S = p.S;
         constexpr int ROWS = 32 * kDqWaves;
-        const int ntq = (S + ROWS - 1) / ROWS;
-        // Heaviest first over the whole grid (under causal masks the last
-        // query rows see the most keys): every head's tile qt, then tile
-        // qt - 1, ... With B*H a multiple of 8, all tiles of a head land on
-        // one XCD (consecutive workgroups go to consecutive XCDs) and share
-        // its L2.
-        const int BH = p.B * p.H;
-        const int bh = (int)blockIdx.x % BH;
-        const int qt = ntq - 1 - (int)blockIdx.x / BH;
         const int q0 = qt * ROWS, qi = q0 + 32 * wave + l32;
         const int64_t head = (int64_t)bh * S * D;
         const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
@@ -321,17 +328,26 @@ struct Bwd {
     static constexpr uint32_t kKvV = 32 * kKvWaves * GQ::RB;
     static constexpr uint32_t kKvStage = 4 * GQ::TILE_BYTES + 2 * QB * 4;
 
+    // The workgroup's items from its work list, as in dq; level l is key
+    // tile ntk - 1 - l (under causal masks the first keys see the most rows).
     static __device__ void dkdv(const BwdParams &p, LDS char *smem) {
+        const int ntk = (p.S + kBwdRows - 1) / kBwdRows;
+        for (int r = 0;; ++r) {
+            int x, bh, l;
+            const int pos = list_pos(p.kv_plan, r, x);
+            if (!list_item(p.kv_plan, x, pos, bh, l)) break;
+            if (r) __syncthreads();
+            dkdv_item(p, smem, __builtin_amdgcn_readfirstlane(bh),
+                      __builtin_amdgcn_readfirstlane(ntk - 1 - l));
+        }
+    }
+    static __device__ __forceinline__ void dkdv_item(const BwdParams &p, LDS char *smem, int bh,
+                                                     int kt) {
         const int lane = threadIdx.x & 63;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const int l32 = lane & 31, g = lane >> 5;
         const int S = p.S;
         constexpr int ROWS = 32 * kKvWaves;
-        // Heaviest first over the whole grid, as in dq (under causal masks
-        // the first keys see the most rows).
-        const int BH = p.B * p.H;
-        const int bh = (int)blockIdx.x % BH;
-        const int kt = (int)blockIdx.x / BH;
         const int k0 = kt * ROWS, kj = k0 + 32 * wave + l32;
         const int64_t head = (int64_t)bh * S * D;
         const uint16_t *qh = static_cast<const uint16_t *>(p.q) + head;
@@ -519,14 +535,11 @@ hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_rowdot_kernel<T, D>),
                                    dim3((unsigned)rd_blocks), dim3(256), args, 0, stream);
     if (e != hipSuccess) return e;
-    const int64_t bh = (int64_t)p.B * p.H;
-    const int64_t kv_tiles = bh * ((p.S + 32 * kKvWaves - 1) / (32 * kKvWaves));
     e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_kernel<T, D>),
-                        dim3((unsigned)kv_tiles), dim3(64 * kKvWaves), args, 0, stream);
+                        dim3((unsigned)p.kv_plan.grid), dim3(64 * kKvWaves), args, 0, stream);
     if (e != hipSuccess) return e;
-    const int64_t q_tiles = bh * ((p.S + 32 * kDqWaves - 1) / (32 * kDqWaves));
     return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D>),
-                           dim3((unsigned)q_tiles), dim3(64 * kDqWaves), args, 0, stream);
+                           dim3((unsigned)p.dq_plan.grid), dim3(64 * kDqWaves), args, 0, stream);
 }
 
 }  // namespace

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_internal.h"
+
 namespace fa {
 namespace dev {
 
@@ -241,6 +243,41 @@ __device__ __forceinline__ void rope_fragments(typename Elem<T>::vec8 (&x)[D / 1
             }
         }
     }
+}
+
+// ---- persistent work lists (ListPlan) ------------------------------------------
+// The list position of this workgroup's item in round r, and its list x.
+__device__ __forceinline__ int list_pos(const ListPlan &pl, int r, int &x) {
+    const int w = blockIdx.x;
+    int j = w, nj = (int)gridDim.x;
+    x = 0;
+    if (pl.xcd_lists) {
+        x = w & 7;
+        j = w >> 3;
+        nj = (int)gridDim.x >> 3;
+    }
+    return r * nj + ((r & 1) ? nj - 1 - j : j);
+}
+// Position pos of list x -> head bh and level; false past the list's end.
+__device__ __forceinline__ bool list_item(const ListPlan &pl, int x, int pos, int &bh,
+                                          int &level) {
+    if (pos >= pl.list_len) return false;
+    int hl;
+    if (pos < pl.flat_items) {
+        const int nf = pl.n_flat;
+        hl = pos / nf;
+        level = pl.levels - 1 - (pos - hl * nf);
+    } else {
+        const int rp = pos - pl.flat_items;
+        const int nq = pl.levels - pl.n_flat;  // levels below the flat part
+        const int gh = pl.group_heads;
+        const int per_group = gh * nq;
+        const int grp = rp / per_group, within = rp - grp * per_group;
+        level = nq - 1 - within / gh;
+        hl = grp * gh + within % gh;
+    }
+    bh = pl.xcd_lists ? hl * 8 + x : hl;
+    return true;
 }
 
 }  // namespace dev

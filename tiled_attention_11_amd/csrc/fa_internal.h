@@ -11,6 +11,32 @@ namespace fa {
 // small enough that i + kUnbounded does not overflow a 32-bit int.
 constexpr int kUnbounded = 1 << 30;
 
+// Persistent-grid work lists, shared by the forward and backward kernels.
+// `grid` workgroups (at most one per CU) each run a stream of items r = 0, 1,
+// ...; an item is one tile (a level: 0 .. levels - 1) of one head, and a
+// head's item costs are expected to grow with the level. xcd_lists: B*H % 8
+// == 0 (packed: H % 8 == 0) and grid % 8 == 0, so list x (heads x, x + 8, ...)
+// is served by workgroups w = x mod 8, which the dispatcher places on XCD x;
+// otherwise one list holds every head. list_len: items per list. Round r
+// hands list positions r*nj .. r*nj + nj - 1 to the list's nj workgroups,
+// reversed on odd rounds (a snake). Positions: first the flat part (n_flat >
+// 0: the last n_flat levels of every head cost the same, the most), head
+// after head, each head's from the last level down (flat_items = heads in
+// the list * n_flat); then the other levels in groups of group_heads heads
+// (dividing the list's heads), each group's levels from the last to the
+// first, the group's heads interleaved, so that a round of the snake pairs a
+// group's costliest item with its cheapest and the workgroups of a list
+// share few heads (and their L2) at a time.
+struct ListPlan {
+    int grid;
+    int xcd_lists;
+    int list_len;
+    int levels;
+    int group_heads;
+    int n_flat;
+    int flat_items;
+};
+
 // Everything a kernel needs, computed and validated on the host.
 struct FwdParams {
     const void *q, *k, *v;  // [B, H, S, D], or packed [T, H, D] (see row addressing)
@@ -23,22 +49,10 @@ struct FwdParams {
     int win_lo, win_hi;
     float c2;               // max(|scale| * log2(e), 2^-100): scores go to base 2 in one multiply
     int negate_q;           // scale < 0: Q's sign is flipped on load instead
-    // Work distribution (see the kernel): `grid` workgroups, each running a
-    // stream of work items (query tiles). xcd_lists: B*H % 8 == 0 (packed: H %
-    // 8 == 0) and grid % 8 == 0, so list x (heads x, x + 8, ...) is served by
-    // workgroups w = x mod 8; otherwise one list holds every head. list_len:
-    // items per list; group_heads: heads per group within a list (divides the
-    // list's heads). Packed sequences order their lists by query tile instead
-    // and use neither. n_flat > 0: the last n_flat query tiles of every head
-    // cost the same (the most) and take the first flat_items = heads in the
-    // list * n_flat positions of a list, head after head; the remaining tiles
-    // (the cheaper ones) follow in groups of group_heads as above.
-    int grid;
-    int xcd_lists;
-    int list_len;
-    int group_heads;
-    int n_flat;
-    int flat_items;
+    // Work distribution: items are query tiles (levels = n_qtiles). Packed
+    // sequences order their lists by query tile (the kernel's walk) and use
+    // only grid and xcd_lists of the plan.
+    ListPlan plan;
     // Row addressing. Row r of head h of sequence b starts at element
     // base + r * row_stride; its LSE at index lse_base + r * lse_stride.
     //   [B, H, S, D]:      base = (b*H + h)*S*D, row_stride = D;
@@ -95,7 +109,14 @@ struct BwdParams {
     int B, H, S;
     int win_lo, win_hi;                // as in FwdParams
     float scale;                       // signed
+    // Work lists: dQ items are 256-row query tiles (level = tile index), dK/dV
+    // items 256-key tiles (level = tiles - 1 - tile index: under causal masks
+    // the first keys are seen by the most rows).
+    ListPlan dq_plan, kv_plan;
 };
+
+// Rows (queries for dQ, keys for dK/dV) of a backward work item.
+constexpr int kBwdRows = 256;
 
 // Enqueue the three backward kernels (row dots, dK/dV, dQ).
 hipError_t launch_bwd(const BwdParams &p, int D, int dtype, hipStream_t stream);

@@ -203,17 +203,11 @@ struct Kernel {
     }
 
     // ---- work items -------------------------------------------------------------
-    // A work item is one query tile (BM rows) of one (b, h). The grid has
-    // at most one workgroup per CU and workgroup w runs its items r = 0, 1, ...
-    // back to back as one stream of key tiles. Items are laid out in lists:
-    // with B*H a multiple of 8, list x holds the heads x, x + 8, x + 16, ... and
-    // is served only by the workgroups w = x (mod 8), which the dispatcher
-    // places on XCD x, so a head's K and V are read into one XCD's L2 and reused
-    // there by all its query tiles. Within a list, heads go in groups of
-    // group_heads, heaviest query tile (longest causal rows) first; round r hands
-    // positions r*nj .. r*nj + nj - 1 to the nj workgroups of the list, in
-    // reverse order on odd rounds, so that a workgroup given a heavy tile in one
-    // round gets a light one in the next.
+    // A work item is one query tile (BM rows) of one (b, h), taken from the
+    // work lists of FwdParams::plan (ListPlan: persistent workgroups, XCD
+    // lists, the snake; under a window the equal-cost tiles first). The grid
+    // has at most one workgroup per CU and workgroup w runs its items r = 0,
+    // 1, ... back to back as one stream of key tiles.
     struct Item {
         int bh, q0;     // head (b*H + h) and first query row
         int t_first;    // first key tile the workgroup's rows can see
@@ -232,51 +226,13 @@ struct Kernel {
         return PACKED ? it.base : (int64_t)it.bh * S_all * D;
     }
 
-    // The workgroup's position in its list: list x (0 without XCD lists),
-    // index j among the list's nj workgroups. Round r takes list position
-    // r * nj + j, or r * nj + nj - 1 - j in odd rounds (a snake, so that the
-    // costliest and the cheapest items of a group pair up).
-    static __device__ __forceinline__ int list_pos(const FwdParams &p, int r, int &x) {
-        const int w = blockIdx.x;
-        int j = w, nj = (int)gridDim.x;
-        x = 0;
-        if (p.xcd_lists) {
-            x = w & 7;
-            j = w >> 3;
-            nj = (int)gridDim.x >> 3;
-        }
-        return r * nj + ((r & 1) ? nj - 1 - j : j);
-    }
-
-    // [B, H, S, D]: list position -> item. Under a sliding window most query
-    // tiles of a head walk the same number of key tiles (the flat part, the
-    // last n_flat tiles): those come first, head after head, each head's from
-    // the last tile down, and the snake deals them out evenly whatever their
-    // order. Then (or from the start, n_flat = 0) a list runs its heads in
-    // groups of group_heads, each group's remaining query tiles from the last
-    // to the first, the group's heads interleaved: a round of the snake then
-    // pairs a group's costliest tile with its cheapest.
     static __device__ __forceinline__ Item item_of(const FwdParams &p, int r) {
         Item it;
-        int x;
-        const int pos = list_pos(p, r, x);
         it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = 0;
-        if (pos >= p.list_len) return it;
-        int qt, hl;
-        if (pos < p.flat_items) {
-            const int nf = p.n_flat;
-            hl = pos / nf;
-            qt = p.n_qtiles - 1 - (pos - hl * nf);
-        } else {
-            const int rp = pos - p.flat_items;
-            const int nq = p.n_qtiles - p.n_flat;  // tiles below the flat part
-            const int gh = p.group_heads;
-            const int per_group = gh * nq;
-            const int grp = rp / per_group, within = rp - grp * per_group;
-            qt = nq - 1 - within / gh;
-            hl = grp * gh + within % gh;
-        }
-        it.bh = p.xcd_lists ? hl * 8 + x : hl;
+        int x, bh, qt;
+        const int pos = list_pos(p.plan, r, x);
+        if (!list_item(p.plan, x, pos, bh, qt)) return it;
+        it.bh = bh;
         it.q0 = qt * BM;
         finish_item(p, it, p.S);
         return it;
@@ -330,8 +286,8 @@ struct Kernel {
         it.bh = it.q0 = it.t_first = it.nt = it.t_in_lo = it.t_in_hi = it.S = 0;
         it.base = 0;
         int x;
-        const int pos = list_pos(p, r, x);
-        const int hpl = p.xcd_lists ? p.H >> 3 : p.H;  // heads per sequence in a list
+        const int pos = list_pos(p.plan, r, x);
+        const int hpl = p.plan.xcd_lists ? p.H >> 3 : p.H;  // heads per sequence in a list
         while (pos >= wk.begin + wk.count) {
             if (wk.lvl == 0) return it;  // past the last level: no more items
             wk.begin += wk.count;
@@ -343,7 +299,7 @@ struct Kernel {
         const int b = active_select(tab, p.B, wk.lvl, k);
         const int start = __builtin_amdgcn_readfirstlane(tab[b].x);
         const int S = __builtin_amdgcn_readfirstlane(tab[b].y);
-        const int h = p.xcd_lists ? i * 8 + x : i;
+        const int h = p.plan.xcd_lists ? i * 8 + x : i;
         it.bh = b * p.H + h;
         it.q0 = wk.lvl * BM;
         it.S = S;
@@ -1240,7 +1196,7 @@ hipError_t launch_t(const FwdParams &p, hipStream_t stream) {
                              : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, true, false>))
         : p.key_split ? reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, false, true>)
                       : reinterpret_cast<const void *>(&fa_fwd_kernel<T, D, false, false, false>);
-    return hipLaunchKernel(fn, dim3(p.grid), dim3(kThreads), args, 0, stream);
+    return hipLaunchKernel(fn, dim3(p.plan.grid), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace
