@@ -122,6 +122,10 @@ fa::ListPlan plan_lists(uint64_t bh, uint64_t levels, bool xcd_ok, int n_cu,
     pl.group_heads = (int)gh;
     pl.n_flat = (int)n_flat;
     pl.flat_items = (int)(list_heads * n_flat);
+    pl.group_shift = 0;
+    while ((1ull << pl.group_shift) < gh) ++pl.group_shift;
+    fa::div_magic(n_flat ? (uint32_t)n_flat : 1u, &pl.flat_m, &pl.flat_s);
+    fa::div_magic((uint32_t)(gh * n_rest), &pl.group_m, &pl.group_s);
     return pl;
 }
 

@@ -262,19 +262,20 @@ __device__ __forceinline__ int list_pos(const ListPlan &pl, int r, int &x) {
 __device__ __forceinline__ bool list_item(const ListPlan &pl, int x, int pos, int &bh,
                                           int &level) {
     if (pos >= pl.list_len) return false;
+    // (the divisions as multiplies and shifts: a runtime integer division
+    // costs a few hundred cycles here, at every item start)
     int hl;
     if (pos < pl.flat_items) {
         const int nf = pl.n_flat;
-        hl = pos / nf;
+        hl = fast_div(pos, pl.flat_m, pl.flat_s);
         level = pl.levels - 1 - (pos - hl * nf);
     } else {
         const int rp = pos - pl.flat_items;
         const int nq = pl.levels - pl.n_flat;  // levels below the flat part
-        const int gh = pl.group_heads;
-        const int per_group = gh * nq;
-        const int grp = rp / per_group, within = rp - grp * per_group;
-        level = nq - 1 - within / gh;
-        hl = grp * gh + within % gh;
+        const int per_group = nq << pl.group_shift;
+        const int grp = fast_div(rp, pl.group_m, pl.group_s), within = rp - grp * per_group;
+        level = nq - 1 - (within >> pl.group_shift);
+        hl = (grp << pl.group_shift) + (within & (pl.group_heads - 1));
     }
     bh = pl.xcd_lists ? hl * 8 + x : hl;
     return true;

@@ -32,10 +32,30 @@ struct ListPlan {
     int xcd_lists;
     int list_len;
     int levels;
-    int group_heads;
+    int group_heads;  // a power of two: log2 in group_shift
     int n_flat;
     int flat_items;
+    int group_shift;
+    // Division by n_flat and by group_heads * (levels - n_flat) as a
+    // multiply and a shift (fast_div; the host sets them with div_magic).
+    uint32_t flat_m, group_m;
+    int flat_s, group_s;
 };
+
+// floor(n / d) for 0 <= n < 2^31 as (n * m) >> s, with m, s from
+// div_magic(d) (Granlund and Montgomery, "Division by invariant integers
+// using multiplication", 1994: with l = ceil(log2 d) and m = floor(2^(31+l)
+// / d) + 1, 2^(31+l) < m d <= 2^(31+l) + 2^l, which makes the quotient exact
+// for every 31-bit n; m < 2^32).
+inline void div_magic(uint32_t d, uint32_t *m, int *s) {
+    int l = 0;
+    while (l < 32 && (1ull << l) < d) ++l;
+    *s = 31 + l;
+    *m = (uint32_t)((1ull << *s) / d + 1);
+}
+__host__ __device__ inline int fast_div(int n, uint32_t m, int s) {
+    return (int)(((uint64_t)(uint32_t)n * m) >> s);
+}
 
 // Everything a kernel needs, computed and validated on the host.
 struct FwdParams {
