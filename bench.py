@@ -513,7 +513,7 @@ def bench_bwd(args, name):
         "dtype": dtype,
         "data": "synthetic",
         "config": {
-            "workload": (f"{name}: fa_bwd (row dots + dK/dV kernel + dQ kernel) at B={B} H={H} "
+            "workload": (f"{name}: fa_bwd (dQ kernel with the row dots + dK/dV kernel) at B={B} H={H} "
                          f"S={S} D={D} {dtype} {w['mask']} scale={w['scale']:.6g}, dO standard "
                          "normal; O and LSE from fa_fwd outside the timed region"),
             "B": B, "H": H, "S": S, "D": D, "mask": w["mask"], "window": [wl, wr],

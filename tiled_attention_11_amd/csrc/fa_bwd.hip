@@ -13,9 +13,9 @@
 // recomputed tile by tile and, as in the forward, no S x S matrix reaches
 // memory.
 //
-// gfx950 design: three kernels.
-//  * fa_bwd_rowdot: D_i = dO_i . O_i (fp32) into the caller's workspace.
-//  * fa_bwd_dq: a workgroup of 8 waves owns 256 query rows (32 per wave, a
+// gfx950 design: two kernels, dQ then dK/dV.
+//  * fa_bwd_dq: first D_i = dO_i . O_i (fp32) for its rows, into the caller's
+//    workspace. A workgroup of 8 waves owns 256 query rows (32 per wave, a
 //    row per lane as in the forward) and streams the visible 64-key tiles of
 //    K and V through LDS (direct HBM -> LDS DMA, two stages). Per 32-key
 //    block: S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16 (Q^T, dO^T
@@ -232,7 +232,21 @@ struct Bwd {
         load_frags(qh, qi, S, g, qf);
         load_frags(doh, qi, S, g, df);
         const float lse2 = qi < S ? p.lse[(int64_t)bh * S + qi] * kLog2e : 0.0f;
-        const float drow = qi < S ? p.rowdot[(int64_t)bh * S + qi] : 0.0f;
+        // D_i = dO_i . O_i in fp32: this lane's half of the row's dims (the
+        // dO fragments it holds), then its partner's (lane ^ 32); written to
+        // the workspace for the dK/dV kernel, which runs after this one.
+        float drow;
+        {
+            vec8 of[NDC];
+            load_frags(static_cast<const uint16_t *>(p.o) + head, qi, S, g, of);
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NDC; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf((float)df[c][e], (float)of[c][e], acc);
+            drow = acc + __shfl_xor(acc, 32);
+            if (qi < S && g == 0) p.rowdot[(int64_t)bh * S + qi] = drow;
+        }
         const float c2 = p.scale * kLog2e;
 
         const int qlast = min(q0 + ROWS - 1, S - 1);
@@ -502,44 +516,16 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void fa_bwd_dkdv_kernel(BwdParams
     Bwd<T, D>::dkdv(p, (LDS char *)smem);
 }
 
-// D_i = dO_i . O_i in fp32: D/8 threads per row, 8 elements each, summed
-// across the row's threads with lane exchanges.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void fa_bwd_rowdot_kernel(BwdParams p) {
-    typedef typename Elem<T>::vec8 vec8;
-    constexpr int TPR = D / 8;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gid / TPR;
-    const int part = (int)(gid % TPR);
-    const int64_t rows = (int64_t)p.B * p.H * p.S;
-    float acc = 0.0f;
-    if (row < rows) {
-        const int64_t off = row * D + 8 * part;
-        const vec8 a = __builtin_bit_cast(
-            vec8, *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.dout) + off));
-        const vec8 b = __builtin_bit_cast(
-            vec8, *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.o) + off));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-    }
-#pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
-    if (row < rows && part == 0) p.rowdot[row] = acc;
-}
-
 template <typename T, int D>
 hipError_t launch_bwd_t(const BwdParams &p, hipStream_t stream) {
     void *args[] = {const_cast<BwdParams *>(&p)};
-    const int64_t rows = (int64_t)p.B * p.H * p.S;
-    const int64_t rd_blocks = (rows * (D / 8) + 255) / 256;
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_rowdot_kernel<T, D>),
-                                   dim3((unsigned)rd_blocks), dim3(256), args, 0, stream);
+    // dQ first: it also writes the row dots D_i that dK/dV reads.
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D>),
+                                   dim3((unsigned)p.dq_plan.grid), dim3(64 * kDqWaves), args, 0,
+                                   stream);
     if (e != hipSuccess) return e;
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_kernel<T, D>),
-                        dim3((unsigned)p.kv_plan.grid), dim3(64 * kKvWaves), args, 0, stream);
-    if (e != hipSuccess) return e;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dq_kernel<T, D>),
-                           dim3((unsigned)p.dq_plan.grid), dim3(64 * kDqWaves), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fa_bwd_dkdv_kernel<T, D>),
+                           dim3((unsigned)p.kv_plan.grid), dim3(64 * kKvWaves), args, 0, stream);
 }
 
 }  // namespace

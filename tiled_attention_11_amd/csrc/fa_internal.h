@@ -138,7 +138,7 @@ struct BwdParams {
 // Rows (queries for dQ, keys for dK/dV) of a backward work item.
 constexpr int kBwdRows = 256;
 
-// Enqueue the three backward kernels (row dots, dK/dV, dQ).
+// Enqueue the two backward kernels (dQ with the row dots, then dK/dV).
 hipError_t launch_bwd(const BwdParams &p, int D, int dtype, hipStream_t stream);
 
 // ---- new query rows against a key/value cache ---------------------------------
