@@ -112,3 +112,44 @@ def test_bwd_headline_shape_two_heads(orc):
             bound = 2 * U["f16"] * m + ulp(r, "f16")
             worst = np.abs(g[sl] - r) / bound
             assert worst.max() <= 1.0, (b, h, name, float(worst.max()))
+
+
+@pytest.mark.parametrize("case", [(4, 16, 2048, 64, "f16", "window", (300, 0)),
+                                  (5, 13, 1300, 64, "bf16", "causal", (-1, -1))],
+                         ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}D{c[3]}{c[4]}{c[5]}")
+def test_bwd_persistent_schedule(orc, case):
+    """Both kernels run persistent workgroups over work lists (XCD lists and,
+    under a window, the equal-cost tiles first; a single list when B*H is not
+    a multiple of 8), several items per workgroup here. Every head's
+    gradients equal that head's gradients computed alone (a launch with a
+    different schedule) bit for bit, so every item ran exactly once; a few
+    heads are also checked against the oracle."""
+    B, H, S, D, dtype, mask, window = case
+    seed = 820 + S
+    say("bwd persistent schedule", case, "seed", seed)
+    q, k, v, do = inputs(B, H, S, D, dtype, seed)
+    scale = 1.0 / math.sqrt(D)
+    tq, tk, tv, tdo = (to_device(x, dtype) for x in (q, k, v, do))
+    # one forward for the batch: a head's forward alone may take another
+    # layout, whose O and LSE differ in the last bits
+    o, lse = fa.forward(tq, tk, tv, scale=scale, mask=mask, window=window)
+
+    def grads(bsl, hsl):
+        parts = [t[bsl, hsl].contiguous() for t in (tq, tk, tv, o, lse, tdo)]
+        out = fa.backward(*parts, scale=scale, mask=mask, window=window)
+        torch.cuda.synchronize()
+        return [decode(to_bits(gr), dtype).reshape(gr.shape) for gr in out]
+
+    got = grads(slice(None), slice(None))
+    for b in range(B):
+        for h in range(H):
+            alone = grads(slice(b, b + 1), slice(h, h + 1))
+            for name, g, a in zip(("dq", "dk", "dv"), got, alone):
+                assert np.array_equal(g[b:b + 1, h:h + 1], a, equal_nan=True), (b, h, name)
+    for b, h in ((0, 0), (B - 1, H - 1), (B // 2, H // 3)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        refs, mags = orc.attention_bwd(q[sl], k[sl], v[sl], do[sl], dtype, scale, mask, window)
+        for name, g, r, m in zip(("dq", "dk", "dv"), got, refs, mags):
+            bound = 2 * U[dtype] * m + ulp(r, dtype)
+            worst = np.abs(g[sl] - r) / bound
+            assert worst.max() <= 1.0, (b, h, name, float(worst.max()))
