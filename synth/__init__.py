@@ -43,6 +43,10 @@ WORKLOADS = {
     "b4h32s4096_causal_rope": dict(B=4, H=32, S=4096, D=128, dtype="f16", mask="causal",
                                    window=(-1, -1), scale=128 ** -0.5, seed=3, rope="halves",
                                    rope_base=10000.0),
+    # one GPU's share of the B4 H32 S4096 causal shape when its heads are
+    # sharded over 8 GPUs (no communication: heads are independent)
+    "b4h4s4096_causal": dict(B=4, H=4, S=4096, D=128, dtype="f16", mask="causal",
+                             window=(-1, -1), scale=128 ** -0.5, seed=3),
     "long_bf16_outliers": dict(B=1, H=64, S=16384, D=128, dtype="bf16", mask="causal",
                                window=(-1, -1), scale=128 ** -0.5, seed=5,
                                outlier_frac=0.01, outlier_scale=20.0),

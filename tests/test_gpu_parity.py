@@ -135,7 +135,7 @@ def test_parity_many_items_per_workgroup(orc, shape, mask, window):
 # D128 causal shape), and those checked on at least 32k rows that include
 # every head's query-tile, key-tile and window edges.
 WHOLE = ("tiny_full", "tiny_causal", "d64_causal", "b4h32s4096_causal",
-         "b4h32s4096_win1024", "b4h32s4096_win1000")
+         "b4h32s4096_win1024", "b4h32s4096_win1000", "b4h4s4096_causal")
 SAMPLED = ("b4h32s4096_full", "long_bf16_outliers", "b4h32s4096_causal_rope")
 HEADS_PER_CHUNK = 16
 _OUT = {}
