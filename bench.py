@@ -118,6 +118,23 @@ def counted_traffic(workload, prefix="fa_fwd", sources=None):
     return int(val.group(1))
 
 
+def c_abi_step(fn, *args):
+    """One timed step: a direct call of a C ABI entry point (the binding of the
+    same name) with its arguments bound once (raw device addresses and the
+    stream handle), so that the host loop costs one ctypes call per launch
+    rather than the argument checks of the torch wrappers, which the first,
+    untimed call of each benchmark still goes through. On short kernels those
+    checks (and the device context they set up) can outlast the kernel and
+    starve the GPU between launches."""
+    import tiled_attention_11_amd as fa
+
+    def step():
+        status = fn(*args)
+        if status != 0:
+            raise fa.FaError(status, fn.__name__)
+    return step
+
+
 def visible_per_row(S, mask, window, rows_i):
     """Visible keys of each query position (for FLOP accounting)."""
     import numpy as np
@@ -226,13 +243,21 @@ def bench_decode(args, name):
     print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s, workspace "
           f"{need} B", file=sys.stderr, flush=True)
 
-    def step():
-        if ps:
-            fa.decode_paged(tq, tkp, tvp, ttab, tlen, Sk, scale=w["scale"], mask=w["mask"],
-                            window=(wl, wr), out=out, lse=lse, workspace=ws)
-        else:
-            fa.decode(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
-                      lse=lse, workspace=ws)
+    code = fa.FA_DTYPE_FP16 if dtype == "f16" else fa.FA_DTYPE_BF16
+    sh = torch.cuda.current_stream().cuda_stream
+    if ps:
+        fa.decode_paged(tq, tkp, tvp, ttab, tlen, Sk, scale=w["scale"], mask=w["mask"],
+                        window=(wl, wr), out=out, lse=lse, workspace=ws)
+        step = c_abi_step(fa.fa_decode_paged, tq.data_ptr(), tkp.data_ptr(), tvp.data_ptr(),
+                          out.data_ptr(), lse.data_ptr(), ttab.data_ptr(), tlen.data_ptr(), B, H,
+                          Sq, Sk, D, tkp.shape[0], tkp.shape[1], ttab.shape[1],
+                          float(w["scale"]), m, wl, wr, code, ws.data_ptr(), ws.numel(), sh)
+    else:
+        fa.decode(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
+                  lse=lse, workspace=ws)
+        step = c_abi_step(fa.fa_decode, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(),
+                          out.data_ptr(), lse.data_ptr(), B, H, Sq, Sk, D, float(w["scale"]), m,
+                          wl, wr, code, ws.data_ptr(), ws.numel(), sh)
 
     for _ in range(args.warmup):
         step()
@@ -347,9 +372,13 @@ def bench_varlen(args, name):
     print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s, lengths "
           f"{lengths.tolist()}", file=sys.stderr, flush=True)
 
-    def step():
-        fa.forward_varlen(tq, tk, tv, tcu, max_seqlen, scale=w["scale"], mask=w["mask"],
-                          window=(wl, wr), out=out, lse=lse)
+    fa.forward_varlen(tq, tk, tv, tcu, max_seqlen, scale=w["scale"], mask=w["mask"],
+                      window=(wl, wr), out=out, lse=lse)
+    step = c_abi_step(fa.fa_fwd_varlen, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(),
+                      out.data_ptr(), lse.data_ptr(), tcu.data_ptr(), len(lengths), max_seqlen,
+                      T, H, D, float(w["scale"]), m, wl, wr,
+                      fa.FA_DTYPE_FP16 if dtype == "f16" else fa.FA_DTYPE_BF16,
+                      torch.cuda.current_stream().cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -474,9 +503,13 @@ def bench_bwd(args, name):
     print(f"[bench] {name}: inputs and forward ready in {time.perf_counter() - t0:.1f}s",
           file=sys.stderr, flush=True)
 
-    def step():
-        fa.backward(tq, tk, tv, o, lse, tdo, scale=w["scale"], mask=w["mask"], window=(wl, wr),
-                    dq=dq, dk=dk, dv=dv, workspace=ws)
+    fa.backward(tq, tk, tv, o, lse, tdo, scale=w["scale"], mask=w["mask"], window=(wl, wr),
+                dq=dq, dk=dk, dv=dv, workspace=ws)
+    step = c_abi_step(fa.fa_bwd, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), o.data_ptr(),
+                      lse.data_ptr(), tdo.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                      dv.data_ptr(), B, H, S, D, float(w["scale"]), m, wl, wr,
+                      fa.FA_DTYPE_FP16 if dtype == "f16" else fa.FA_DTYPE_BF16, ws.data_ptr(),
+                      ws.numel(), torch.cuda.current_stream().cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -613,13 +646,22 @@ def main():
     print(f"[bench] {name}: inputs ready in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
 
-    def step():
-        if rope:
-            fa.forward_rope(tq, tk, tv, tcos, tsin, mode=rope, k_rot=k_rot, scale=w["scale"],
-                            mask=w["mask"], window=(wl, wr), out=out, lse=lse)
-        else:
-            fa.forward(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
-                       lse=lse)
+    code = fa.FA_DTYPE_FP16 if dtype == "f16" else fa.FA_DTYPE_BF16
+    mcode = fa._mask_code(w["mask"])
+    sh = torch.cuda.current_stream().cuda_stream
+    if rope:
+        fa.forward_rope(tq, tk, tv, tcos, tsin, mode=rope, k_rot=k_rot, scale=w["scale"],
+                        mask=w["mask"], window=(wl, wr), out=out, lse=lse)
+        step = c_abi_step(fa.fa_fwd_rope, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(),
+                          out.data_ptr(), lse.data_ptr(), k_rot.data_ptr(), tcos.data_ptr(),
+                          tsin.data_ptr(), tcos.shape[0], fa._rope_code(rope), B, H, S, D,
+                          float(w["scale"]), mcode, wl, wr, code, sh)
+    else:
+        fa.forward(tq, tk, tv, scale=w["scale"], mask=w["mask"], window=(wl, wr), out=out,
+                   lse=lse)
+        step = c_abi_step(fa.fa_fwd, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(),
+                          out.data_ptr(), lse.data_ptr(), B, H, S, D, float(w["scale"]), mcode,
+                          wl, wr, code, sh)
 
     for _ in range(args.warmup):
         step()

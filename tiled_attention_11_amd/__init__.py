@@ -262,6 +262,27 @@ def _mask_code(mask):
         raise ValueError(f"mask must be one of {sorted(_MASKS)}, got {mask!r}") from None
 
 
+class _Nothing:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+_NOTHING = _Nothing()
+
+
+def _on_device(device):
+    """A context that makes ``device`` current for the library call; nothing
+    to do (and no device switch) when it already is, the common case."""
+    import torch
+
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _NOTHING
+    return torch.cuda.device(device)
+
+
 def forward(q, k, v, *, scale=None, mask="full", window=(-1, -1), out=None, lse=None,
             return_lse=True, stream=None):
     """Attention forward on torch device tensors.
@@ -299,7 +320,7 @@ def forward(q, k, v, *, scale=None, mask="full", window=(-1, -1), out=None, lse=
     dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         status = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                         lse.data_ptr() if lse is not None else None, B, H, S, D,
                         float(scale), _mask_code(mask), int(wl), int(wr), dtype, stream)
@@ -349,7 +370,7 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, *, scale=None, mask="full",
     dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         status = fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr() if lse is not None else None,
                                cu_seqlens.data_ptr(), nseq, int(max_seqlen), T, H, D,
@@ -397,7 +418,7 @@ def rope(x, cos, sin, *, mode="halves", out=None, stream=None):
     dtype = FA_DTYPE_FP16 if x.dtype == torch.float16 else FA_DTYPE_BF16
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    with torch.cuda.device(x.device):
+    with _on_device(x.device):
         status = fa_rope(x.data_ptr(), out.data_ptr(), cos.data_ptr(), sin.data_ptr(),
                          cos.shape[0], _rope_code(mode), B, H, S, D, dtype, stream)
     if status != 0:
@@ -442,7 +463,7 @@ def forward_rope(q, k, v, cos, sin, *, mode="halves", k_rot=None, scale=None, ma
     dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         status = fa_fwd_rope(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              lse.data_ptr() if lse is not None else None, k_rot.data_ptr(),
                              cos.data_ptr(), sin.data_ptr(), cos.shape[0], _rope_code(mode),
@@ -493,7 +514,7 @@ def backward(q, k, v, o, lse, dout, *, scale=None, mask="full", window=(-1, -1),
     dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         status = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                         dout.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
                         grads[2].data_ptr(), B, H, S, D, float(scale), _mask_code(mask),
@@ -546,7 +567,7 @@ def decode(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=None, lse
     wl, wr = window
     m = _mask_code(mask)
     dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         need = fa_decode_workspace_bytes(B, H, Sq, Sk, D, m, int(wl), int(wr))
         if need < 0:
             raise FaError(int(need), "fa_decode")
@@ -609,7 +630,7 @@ def decode_noalloc(q, k, v, *, scale=None, mask="causal", window=(-1, -1), out=N
     wl, wr = window
     m = _mask_code(mask)
     dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
         status = fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -659,7 +680,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, max_seq_len, *, sca
     wl, wr = window
     m = _mask_code(mask)
     dtype = FA_DTYPE_FP16 if q.dtype == torch.float16 else FA_DTYPE_BF16
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         need = fa_decode_paged_workspace_bytes(B, H, Sq, int(max_seq_len), D, m, int(wl), int(wr))
         if need < 0:
             raise FaError(int(need), "fa_decode_paged")
