@@ -124,6 +124,23 @@ int64_t fa_visible_pairs(int S, int mask_mode, int win_l, int win_r);
 int64_t fa_fwd_flops(int B, int H, int S, int D, int mask_mode, int win_l, int win_r);
 
 /*
+ * fa_fwd_schedule -- the work plan fa_fwd uses for these arguments on a GPU
+ * with n_cu compute units, without launching anything (host only; for tests
+ * and tools). The query rows of each head are cut into work items (256 rows,
+ * or 128 under the key-split layout of small grids); a persistent grid of
+ * workgroups runs them from per-XCD lists in snake order (the tile-fusion
+ * page's host-side grid and its causal block skipping, Ascend C
+ * FlashAttention-2 page, sections 6 and 7, applied per item). Writes up to
+ * max_items entries of 6 int32 each to `items` (host memory, caller-owned;
+ * may be NULL when max_items is 0): workgroup, round, head b*H + h, first
+ * query row, rows per item, key tiles the item walks. Returns the number of
+ * entries (which may exceed max_items), or a negative fa_status for the
+ * argument errors fa_fwd would report (pointer checks aside).
+ */
+int64_t fa_fwd_schedule(int B, int H, int S, int D, int mask_mode, int win_l, int win_r,
+                        int n_cu, int32_t *items, int64_t max_items);
+
+/*
  * fa_fwd_varlen -- fa_fwd over a batch of sequences of different lengths
  * packed token after token: sequence b holds tokens cu_seqlens[b] ..
  * cu_seqlens[b+1] - 1 of the packed tensors and attends only within itself,

@@ -22,7 +22,7 @@ import os
 __all__ = [
     "FA_MASK_FULL", "FA_MASK_CAUSAL", "FA_MASK_WINDOW", "FA_DTYPE_FP16",
     "FA_DTYPE_BF16", "FaError", "fa_fwd", "fa_visible_pairs", "fa_fwd_flops",
-    "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_rope", "fa_fwd_rope", "FA_ROPE_HALVES",
+    "fa_fwd_schedule", "fa_fwd_varlen", "fa_fwd_varlen_flops", "fa_rope", "fa_fwd_rope", "FA_ROPE_HALVES",
     "FA_ROPE_INTERLEAVED", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_flops", "fa_decode",
     "fa_decode_rope", "fa_decode_paged_rope", "fa_decode_workspace_bytes", "fa_decode_flops", "fa_decode_paged",
     "fa_decode_paged_workspace_bytes", "fa_decode_noalloc", "fa_strerror", "forward",
@@ -65,6 +65,8 @@ def _load(path=None):
     lib.fa_visible_pairs.restype = ctypes.c_int64
     lib.fa_fwd_flops.argtypes = [ci, ci, ci, ci, ci, ci, ci]
     lib.fa_fwd_flops.restype = ctypes.c_int64
+    lib.fa_fwd_schedule.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, vp, ctypes.c_int64]
+    lib.fa_fwd_schedule.restype = ctypes.c_int64
     i64 = ctypes.c_int64
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float,
                                   ci, ci, ci, ci, vp]
@@ -145,6 +147,23 @@ def fa_visible_pairs(S, mask_mode, win_l=-1, win_r=-1):
 
 def fa_fwd_flops(B, H, S, D, mask_mode, win_l=-1, win_r=-1):
     return _lib.fa_fwd_flops(B, H, S, D, mask_mode, win_l, win_r)
+
+
+def fa_fwd_schedule(B, H, S, D, mask_mode, win_l, win_r, n_cu):
+    """The forward's work plan on a GPU with ``n_cu`` compute units, as an
+    int32 numpy array of rows (workgroup, round, head, first query row, rows
+    per item, key tiles); raises FaError on bad arguments."""
+    import numpy as np
+
+    n = _lib.fa_fwd_schedule(B, H, S, D, mask_mode, win_l, win_r, n_cu, None, 0)
+    if n < 0:
+        raise FaError(n, "fa_fwd_schedule")
+    out = np.zeros((max(n, 1), 6), dtype=np.int32)
+    m = _lib.fa_fwd_schedule(B, H, S, D, mask_mode, win_l, win_r, n_cu,
+                             out.ctypes.data_as(ctypes.c_void_p), n)
+    if m != n:
+        raise FaError(m if m < 0 else -1, "fa_fwd_schedule")
+    return out[:n]
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen, total_tokens, H, D, scale,

@@ -140,10 +140,7 @@ int64_t tiles_seen(int64_t r0, int64_t r1, int64_t S, int64_t lo, int64_t hi, in
 
 // rows: the sequence length that sets the item count (the longest sequence
 // when packed). allow_split: the layout may use the key-split variant.
-int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int dtype,
-                        hipStream_t stream, bool allow_split) {
-    int n_cu = 0;
-    if (device_cus(&n_cu) != FA_OK) return FA_ERR_HIP;
+void plan_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int n_cu, bool allow_split) {
     // The key split (128-row items, the two wave groups of a workgroup on
     // alternate key tiles, merged at the end) for grids with fewer than two
     // 256-row items per CU: the heaviest causal item then sets the time, and
@@ -169,6 +166,13 @@ int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int
         };
     }
     p.plan = plan_lists(bh, n_qtiles, xcd_ok, n_cu, cost);
+}
+
+int plan_and_launch_fwd(fa::FwdParams &p, uint64_t bh, uint64_t rows, int D, int dtype,
+                        hipStream_t stream, bool allow_split) {
+    int n_cu = 0;
+    if (device_cus(&n_cu) != FA_OK) return FA_ERR_HIP;
+    plan_fwd(p, bh, rows, D, n_cu, allow_split);
     hipError_t err = fa::launch_fwd(p, D, dtype, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -325,6 +329,50 @@ extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, floa
                       int win_r, int dtype, hipStream_t stream) {
     return fwd_core(q, k, v, o, lse, B, H, S, D, scale, mask_mode, win_l, win_r, dtype, stream,
                     nullptr);
+}
+
+extern "C" int64_t fa_fwd_schedule(int B, int H, int S, int D, int mask_mode, int win_l,
+                                   int win_r, int n_cu, int32_t *items, int64_t max_items) {
+    if (B < 0 || H < 0 || S < 0 || n_cu < 1 || max_items < 0) return FA_ERR_INVALID_ARG;
+    int win_lo, win_hi;
+    if (!window_of(mask_mode, win_l, win_r, &win_lo, &win_hi)) return FA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * S == 0) return 0;
+    const uint64_t bh = (uint64_t)B * H;
+    if ((uint64_t)S * D * 2 >= (1ull << 31)) return FA_ERR_TOO_LARGE;
+    if (bh * (((uint64_t)S + fa::kBlockMSplit - 1) / fa::kBlockMSplit) > (uint64_t)INT32_MAX)
+        return FA_ERR_TOO_LARGE;
+    if (max_items > 0 && !items) return FA_ERR_INVALID_ARG;
+    fa::FwdParams p{};
+    p.B = B;
+    p.H = H;
+    p.S = S;
+    p.win_lo = win_lo;
+    p.win_hi = win_hi;
+    p.cu_seqlens = nullptr;
+    plan_fwd(p, bh, (uint64_t)S, D, n_cu, true);
+    const int rows = p.key_split ? fa::kBlockMSplit : fa::kBlockM;
+    const int64_t bn = fa::fwd_key_tile(D);
+    int64_t n = 0;
+    for (int w = 0; w < p.plan.grid; ++w)
+        for (int r = 0;; ++r) {
+            int x, head, level;
+            const int pos = fa::list_pos_at(p.plan, w, p.plan.grid, r, x);
+            if (!fa::list_item(p.plan, x, pos, head, level)) break;
+            if (n < max_items) {
+                const int64_t q0 = (int64_t)level * rows;
+                int32_t *e = items + 6 * n;
+                e[0] = w;
+                e[1] = r;
+                e[2] = head;
+                e[3] = (int32_t)q0;
+                e[4] = rows;
+                e[5] = (int32_t)tiles_seen(q0, std::min<int64_t>(q0 + rows - 1, S - 1), S,
+                                           win_lo, win_hi, bn);
+            }
+            ++n;
+        }
+    return n;
 }
 
 extern "C" int fa_fwd_rope(const void *q, const void *k, const void *v, void *o, float *lse,

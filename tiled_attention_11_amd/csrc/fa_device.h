@@ -246,39 +246,10 @@ __device__ __forceinline__ void rope_fragments(typename Elem<T>::vec8 (&x)[D / 1
 }
 
 // ---- persistent work lists (ListPlan) ------------------------------------------
-// The list position of this workgroup's item in round r, and its list x.
+// The list position of this workgroup's item in round r, and its list x
+// (list_pos_at and list_item in fa_internal.h, shared with the host).
 __device__ __forceinline__ int list_pos(const ListPlan &pl, int r, int &x) {
-    const int w = blockIdx.x;
-    int j = w, nj = (int)gridDim.x;
-    x = 0;
-    if (pl.xcd_lists) {
-        x = w & 7;
-        j = w >> 3;
-        nj = (int)gridDim.x >> 3;
-    }
-    return r * nj + ((r & 1) ? nj - 1 - j : j);
-}
-// Position pos of list x -> head bh and level; false past the list's end.
-__device__ __forceinline__ bool list_item(const ListPlan &pl, int x, int pos, int &bh,
-                                          int &level) {
-    if (pos >= pl.list_len) return false;
-    // (the divisions as multiplies and shifts: a runtime integer division
-    // costs a few hundred cycles here, at every item start)
-    int hl;
-    if (pos < pl.flat_items) {
-        const int nf = pl.n_flat;
-        hl = fast_div(pos, pl.flat_m, pl.flat_s);
-        level = pl.levels - 1 - (pos - hl * nf);
-    } else {
-        const int rp = pos - pl.flat_items;
-        const int nq = pl.levels - pl.n_flat;  // levels below the flat part
-        const int per_group = nq << pl.group_shift;
-        const int grp = fast_div(rp, pl.group_m, pl.group_s), within = rp - grp * per_group;
-        level = nq - 1 - (within >> pl.group_shift);
-        hl = (grp << pl.group_shift) + (within & (pl.group_heads - 1));
-    }
-    bh = pl.xcd_lists ? hl * 8 + x : hl;
-    return true;
+    return list_pos_at(pl, (int)blockIdx.x, (int)gridDim.x, r, x);
 }
 
 }  // namespace dev

@@ -57,6 +57,41 @@ __host__ __device__ inline int fast_div(int n, uint32_t m, int s) {
     return (int)(((uint64_t)(uint32_t)n * m) >> s);
 }
 
+// Workgroup w of `grid`: the list position of its item in round r (the
+// snake), and its list x.
+__host__ __device__ inline int list_pos_at(const ListPlan &pl, int w, int grid, int r, int &x) {
+    int j = w, nj = grid;
+    x = 0;
+    if (pl.xcd_lists) {
+        x = w & 7;
+        j = w >> 3;
+        nj = grid >> 3;
+    }
+    return r * nj + ((r & 1) ? nj - 1 - j : j);
+}
+// Position pos of list x -> head bh and level; false past the list's end.
+// (The divisions are multiplies and shifts: a runtime integer division
+// costs a few hundred cycles on the GPU, at every item start.)
+__host__ __device__ inline bool list_item(const ListPlan &pl, int x, int pos, int &bh,
+                                          int &level) {
+    if (pos >= pl.list_len) return false;
+    int hl;
+    if (pos < pl.flat_items) {
+        const int nf = pl.n_flat;
+        hl = fast_div(pos, pl.flat_m, pl.flat_s);
+        level = pl.levels - 1 - (pos - hl * nf);
+    } else {
+        const int rp = pos - pl.flat_items;
+        const int nq = pl.levels - pl.n_flat;  // levels below the flat part
+        const int per_group = nq << pl.group_shift;
+        const int grp = fast_div(rp, pl.group_m, pl.group_s), within = rp - grp * per_group;
+        level = nq - 1 - (within >> pl.group_shift);
+        hl = (grp << pl.group_shift) + (within & (pl.group_heads - 1));
+    }
+    bh = pl.xcd_lists ? hl * 8 + x : hl;
+    return true;
+}
+
 // Everything a kernel needs, computed and validated on the host.
 struct FwdParams {
     const void *q, *k, *v;  // [B, H, S, D], or packed [T, H, D] (see row addressing)
