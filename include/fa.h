@@ -100,8 +100,11 @@ typedef enum {
  * needs no workspace and keeps no reference after return. o and lse must not
  * overlap q, k, v or each other (checked on the host).
  * Arithmetic: QK^T and PV run on fp16/bf16 matrix cores with fp32 accumulation;
- * softmax state is fp32; probabilities are rounded once to `dtype` for PV. The
- * row sum (and so the LSE) adds the unrounded fp32 probabilities. Results
+ * softmax state is fp32. For PV the probabilities are rounded once to fp16
+ * (fp16 inputs) or carried as two bf16 terms, the rounded value and the
+ * rounded remainder, each multiplied by V (bf16 inputs: an 8-bit significand
+ * alone is too coarse for the output bound when a few keys dominate a row).
+ * The row sum (and so the LSE) adds the unrounded fp32 probabilities. Results
  * are bitwise deterministic for a given input, device and library build.
  * Returns FA_OK or a negative fa_status.
  */
