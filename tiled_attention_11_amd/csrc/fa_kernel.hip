@@ -13,40 +13,45 @@
 // (lnwmold.com/news/1200460), section "usage".
 //
 // gfx950 design (not the pages' Ascend design):
-//  * One workgroup = 8 waves of 64 lanes = 256 query rows of one (b, h);
-//    each wave owns 32 query rows for the whole key loop. The waves form two
-//    groups (0-3 and 4-7, one wave of each per SIMD) that alternate between
-//    an MFMA phase (P V of the previous key tile, then the scores of the next)
-//    and a VALU phase (mask and online softmax), in opposite order within
-//    each step of the key loop (one workgroup barrier per step), so that on
-//    every SIMD one wave keeps the matrix core busy while the other computes
-//    exponentials: a single wave cannot issue VALU work fast enough to hide
-//    it under its own MFMAs, but two waves of a SIMD co-issue.
+//  * A workgroup is 8 waves of 64 lanes, one per CU, persistent: it runs a
+//    stream of work items from a precomputed list (ListPlan). The lists keep
+//    a head's items on one XCD, put the costliest equal-cost items first
+//    where a mask makes many (windows) and pair costly with cheap ones in a
+//    snake order. An item is 256 query rows of one
+//    (b, h), each wave owning 32 rows for the whole key loop. Small grids use
+//    128-row items (key split): waves w and w + 4 share rows, take alternate
+//    key tiles and merge their softmax states at the end.
+//  * The waves form two groups (0-3 and 4-7, one wave of each per SIMD). The
+//    groups alternate between an MFMA phase (P V of the previous key tile,
+//    then the scores of the next) and a VALU phase (mask and online
+//    softmax), in opposite order within each step of the key loop (one
+//    workgroup barrier per step). On every SIMD one wave keeps the matrix
+//    core busy while the other computes exponentials: a single wave cannot
+//    issue VALU work fast enough to hide it under its own MFMAs, but two
+//    waves of a SIMD co-issue.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16
 //    (A = 32 keys x 16 dims, B = 16 dims x 32 queries). In the accumulator
 //    layout lane l holds query l % 32 and 16 keys, so the row max and row sum
 //    are in-lane reductions plus one v_permlane32_swap with lane l ^ 32, and
 //    the per-row rescale of the output is a per-lane scalar.
-//  * The output is accumulated transposed too, O^T += V^T P^T: P^T comes
-//    straight out of the score accumulator (rounded to fp16/bf16) as the B
-//    operand; the V^T A operand is read from the row-major V tile with the
-//    transposing LDS load ds_read_b64_tr_b16 (a 16-lane group reads a 4 x 16
-//    block and each lane receives one column), so V is never transposed in
-//    registers.
+//  * The output is accumulated transposed too, O^T += V^T P^T. P^T comes
+//    straight out of the score accumulator as the B operand: rounded to fp16,
+//    or for bf16 as two bf16 terms (value and remainder, two products). The
+//    V^T A operand is read from the row-major V tile with the transposing
+//    LDS load ds_read_b64_tr_b16 (a 16-lane group reads a 4 x 16 block and
+//    each lane receives one column), so V is never transposed in registers.
 //  * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds,
 //    16 bytes per lane, hardware zero-fill past the end of the sequence),
-//    double-buffered: each tile has two phases to land. No staging registers,
-//    no staging VALU.
+//    double-buffered. The blocks of a tile are spread over the phase that
+//    issues them. The next item's Q and first K tile stream in during the
+//    current item. No staging registers, no staging VALU.
 //  * LDS tiles are unpadded and XOR-swizzled per row in 16-byte chunks so that
 //    both the 16-byte K reads and the transposing V reads are free of bank
 //    conflicts on the 64-bank gfx950 LDS.
-//  * Key tiles that the mask hides from all 256 rows are never loaded; every
-//    wave walks the same tiles (a tile hidden from a wave's rows is fully
-//    masked for it), fully visible tiles run without mask arithmetic, and only
-//    boundary tiles evaluate the predicate.
-//  * The flat workgroup index is remapped so that all query tiles of a head
-//    land on one XCD (workgroups are dealt round-robin over the 8 XCDs) and
-//    run heaviest-first (longest causal rows first).
+//  * Key tiles that the mask hides from all of an item's rows are never
+//    loaded. A wave skips the phases of tiles hidden from its own rows.
+//    Fully visible tiles run without mask arithmetic; only boundary tiles
+//    evaluate the predicate.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
