@@ -675,9 +675,9 @@ struct Kernel {
                 [&](int b) { dma_block(kt, ad.kdma[b], wave, b); });
         }
         // The MFMA stream of a phase: P V of the tile whose V^T sits at `vs`
-        // (PV), then the scores of the tile whose K sits at `ks` (QK); with
-        // NDMA > 0, dma(b) for b = 0 .. NDMA - 1 is called once every NS / NDMA
-        // MFMAs.
+        // (PV) and the scores of the tile whose K sits at `ks` (QK), one after
+        // the other or (fp16) alternating; with NDMA > 0, dma(b) for b = 0 ..
+        // NDMA - 1 is called once every NS / NDMA MFMAs.
         template <bool QK, bool PV, int NDMA, typename Dma>
         __device__ __forceinline__ void mcore(State &st, f32x16 (&sacc)[NKB], const PBuf &pk,
                                               const LDS char *ks,
@@ -733,16 +733,25 @@ struct Kernel {
                     sacc[kb] = Elem<T>::mma(a[s], st.qf[c], c == 0 ? f32x16{} : sacc[kb]);
                 }
             };
+            // Issue order u -> slot. With both products and a single P term
+            // (fp16), P V and score slots alternate. The scores form only NKB
+            // accumulator chains (two at D = 128). An MFMA waits for the
+            // previous one of its chain for about two MFMA times, so with the
+            // other wave of the SIMD in its softmax, two chains alone leave
+            // the matrix core idle a third of the time; between the P V
+            // products (NDB more chains) they do not.
+            constexpr bool kMix = PV && QK && !kSplitP && NPV == NQK;
+            auto at = [](int u) { return kMix ? ((u & 1) ? NPV + (u >> 1) : (u >> 1)) : u; };
 #pragma unroll
-            for (int s = 0; s < kDist && s < NS; ++s) load(s);
+            for (int u = 0; u < kDist && u < NS; ++u) load(at(u));
             constexpr int kPer = NS / (NDMA > 0 ? NDMA : 1);  // MFMAs per DMA block
             static_assert(NDMA == 0 || kPer * NDMA == NS, "DMA blocks spread evenly");
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (s + kDist < NS) load(s + kDist);
-                mma(s);
+            for (int u = 0; u < NS; ++u) {
+                if (u + kDist < NS) load(at(u + kDist));
+                mma(at(u));
                 if constexpr (NDMA > 0)
-                    if (s % kPer == kPer - 1) dma(s / kPer);
+                    if (u % kPer == kPer - 1) dma(u / kPer);
             }
             // Issue order: the first kDist reads, then per slot its look-ahead
             // read(s) and its MFMA.
@@ -751,10 +760,10 @@ struct Kernel {
                 else if (nreads(s) == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             };
 #pragma unroll
-            for (int s = 0; s < kDist && s < NS; ++s) read_group(s);
+            for (int u = 0; u < kDist && u < NS; ++u) read_group(at(u));
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (s + kDist < NS) read_group(s + kDist);
+            for (int u = 0; u < NS; ++u) {
+                if (u + kDist < NS) read_group(at(u + kDist));
                 __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
             }
             if (QK) pin(sacc);
